@@ -1,0 +1,212 @@
+/*
+ * qlinear.h -- C ABI of libqlinear.so, the MI355X (gfx950) quantized
+ * linear-layer GEMM.
+ *
+ * The operation (restated from "Building a High-Performance and Portable vLLM
+ * Linear Backend with Helion", section "Helion Linear Backend / Scope"):
+ *
+ *   FP8_Dynamic   Y[m,n] = bf16( sA[m] * sB[n] * sum_k A[m,k] * B[n,k] )
+ *                 A, B in OCP e4m3fn; one fp32 scale per activation token m
+ *                 and per weight output channel n.
+ *   W8A8_INT8     the same with int8 A, B (exact int32 accumulation).
+ *   Block_FP8     Y[m,n] = bf16( sum_g sA[m,g] * sB[n/128,g]
+ *                                   * sum_{k in group g} A[m,k] * B[n,k] )
+ *                 e4m3 A, B; one activation scale per 1x128 K group, one
+ *                 weight scale per 128x128 block (groups start at k = 0 and
+ *                 blocks at n = 0).
+ *
+ * Layouts: A is [M rows][lda bytes], B is [N rows][ldb bytes], both
+ * K-contiguous (B is the weight in its [out_features, in_features] form, so
+ * Y = A * B^T).  Y is [M rows][ldy elements] of bfloat16 bit patterns.
+ * Scales are fp32: sA [M] and sB [N] (token/channel), or row-major
+ * sA [M][K/128] and sB [N/128][K/128] (block).
+ *
+ * The same post's "Kernel Implementation" section describes the algorithm
+ * variants exposed here as configuration: Standard, Split-K (K partitioned
+ * across workgroups; here reduced through a workspace in a fixed order, so
+ * results are run-to-run reproducible) and Swap-AB (computing the transposed
+ * product so the small token dimension sits on the matrix core's N side).
+ * The techfeed.io summary of the post gives the tunable domains: split_k is
+ * a power of two from 1 to 256, swap_ab is a boolean.  The kernel, variant,
+ * tiles and split_k are looked up per (format, M, N, K) in a table written
+ * by an offline sweep on the MI355X itself.
+ *
+ * Conventions
+ *  - Ownership: the caller owns every buffer (A, B, scales, Y, workspace);
+ *    all are device pointers.  The library never allocates, frees or
+ *    synchronises on the call path; its only state is the host-side config
+ *    table.
+ *  - Asynchrony: calls enqueue kernels on `stream` (a hipStream_t; NULL is
+ *    the default stream) and return at once.  No host synchronisation, no
+ *    allocation and no memset is issued, so calls may be captured into a
+ *    HIP graph.
+ *  - Errors: argument checks run on the host before any HIP call; a failed
+ *    check returns its status and launches nothing.  A launch failure
+ *    returns QLIN_ERR_HIP.  Device faults surface at the caller's next
+ *    stream synchronisation.
+ *  - Shapes: M >= 0 and N >= 0 (M == 0 or N == 0 returns QLIN_OK with no
+ *    launch); K > 0 and K % 16 == 0; lda, ldb >= K and % 16 == 0; ldy >= N.
+ *    Block_FP8 also needs K % 128 == 0 and N % 128 == 0.  Any M and, for
+ *    token/channel scaling, any N are handled (tails are masked).
+ *  - Alignment: A, B, Y and the workspace 16-byte aligned; scales 4-byte.
+ *  - Workspace: split_k > 1 needs `workspace_bytes >= qlin_workspace_size(..)`
+ *    for the selected config (0 when split_k == 1).  Layout: the first
+ *    128 KiB hold one int32 counter per output tile for the last-arriver
+ *    reduction, then the fp32/int32 split partials [split_k][M][N].  The
+ *    counter region must hold zeros before the first call (allocate the
+ *    workspace zeroed); every completed call leaves it zeroed again, and no
+ *    call writes partials into it, so one workspace serves every config.
+ *    Calls that may overlap in time (different streams) need distinct
+ *    workspaces.
+ *  - Threading: concurrent calls are safe; qlin_load_config_table must not
+ *    run concurrently with calls.
+ */
+#ifndef QLINEAR_H
+#define QLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLINEAR_ABI_VERSION 1
+
+typedef enum qlin_status {
+    QLIN_OK = 0,
+    QLIN_ERR_NULL_POINTER = 1,  /* a required pointer is NULL */
+    QLIN_ERR_BAD_SHAPE = 2,     /* M/N/K out of range or not a required multiple */
+    QLIN_ERR_BAD_STRIDE = 3,    /* lda/ldb/ldy too small or not a required multiple */
+    QLIN_ERR_MISALIGNED = 4,    /* a pointer violates the alignment rules */
+    QLIN_ERR_WORKSPACE = 5,     /* workspace missing or smaller than required */
+    QLIN_ERR_BAD_CONFIG = 6,    /* explicit config not valid / not built for this shape */
+    QLIN_ERR_CONFIG_FILE = 7,   /* config table file unreadable or malformed */
+    QLIN_ERR_HIP = 8,           /* a HIP call or kernel launch failed */
+    QLIN_ERR_BAD_ARGUMENT = 9   /* unknown enum value */
+} qlin_status;
+
+typedef enum qlin_dtype {
+    QLIN_E4M3 = 0,              /* OCP e4m3fn bytes */
+    QLIN_INT8 = 1               /* two's-complement int8 bytes */
+} qlin_dtype;
+
+typedef enum qlin_scaling {
+    QLIN_TOKEN_CHANNEL = 0,     /* sA [M], sB [N] */
+    QLIN_BLOCK128 = 1           /* sA [M][K/128], sB [N/128][K/128]; e4m3 only */
+} qlin_scaling;
+
+typedef enum qlin_kernel {
+    QLIN_KERNEL_STREAM = 0,     /* weights streamed HBM -> registers; small M */
+    QLIN_KERNEL_TILE = 1        /* A and B tiles staged through a double-buffered LDS ring; large M */
+} qlin_kernel;
+
+typedef enum qlin_variant {
+    QLIN_STANDARD = 0,          /* matrix-core rows = tokens, columns = weights */
+    QLIN_SWAP_AB = 1            /* computes Y^T = B A^T: rows = weights, columns = tokens */
+} qlin_variant;
+
+typedef enum qlin_reduce {
+    QLIN_REDUCE_TWO_PASS = 0,   /* split partials summed by a second kernel */
+    QLIN_REDUCE_LAST_ARRIVER = 1 /* summed in-kernel by the last split to finish */
+} qlin_reduce;
+
+/* One launch configuration.  For the STREAM kernel: tile_m = tokens per
+ * workgroup (16 or 32), tile_n = weight rows per workgroup, tile_k = K bytes
+ * each wave loads per pipeline step (multiple of 128), waves_n x waves_k
+ * waves split the tile's rows and the split's K range.  For the TILE kernel:
+ * tile_m x tile_n output tile, tile_k = 128, waves_n x waves_k is the wave
+ * grid over the tile (rows x columns).  split_k is 1..256, a power of two;
+ * each split covers a contiguous, 128-aligned K range.  stages is the
+ * pipeline depth (2). */
+typedef struct qlin_config {
+    int32_t kernel;     /* qlin_kernel */
+    int32_t variant;    /* qlin_variant */
+    int32_t tile_m;
+    int32_t tile_n;
+    int32_t tile_k;
+    int32_t waves_n;
+    int32_t waves_k;
+    int32_t stages;
+    int32_t split_k;
+    int32_t reduce;     /* qlin_reduce */
+} qlin_config;
+
+/* FP8_Dynamic (dt = QLIN_E4M3) and W8A8_INT8 (dt = QLIN_INT8) with per-token
+ * a_scale[M] and per-channel b_scale[N].  Config from the table. */
+qlin_status qlin_scaled_mm(qlin_dtype dt, int64_t M, int64_t N, int64_t K,
+                           const void *A, int64_t lda, const float *a_scale,
+                           const void *B, int64_t ldb, const float *b_scale,
+                           void *Y, int64_t ldy,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Block_FP8: e4m3 A and B, a_scale [M][K/128], b_scale [N/128][K/128]. */
+qlin_status qlin_block_scaled_mm(int64_t M, int64_t N, int64_t K,
+                                 const void *A, int64_t lda, const float *a_scale,
+                                 const void *B, int64_t ldb, const float *b_scale,
+                                 void *Y, int64_t ldy,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* The same two operations with an explicit configuration (tuning, tests).
+ * cfg must name a built kernel instance; otherwise QLIN_ERR_BAD_CONFIG. */
+qlin_status qlin_scaled_mm_cfg(qlin_dtype dt, int64_t M, int64_t N, int64_t K,
+                               const void *A, int64_t lda, const float *a_scale,
+                               const void *B, int64_t ldb, const float *b_scale,
+                               void *Y, int64_t ldy,
+                               void *workspace, size_t workspace_bytes, void *stream,
+                               const qlin_config *cfg);
+qlin_status qlin_block_scaled_mm_cfg(int64_t M, int64_t N, int64_t K,
+                                     const void *A, int64_t lda, const float *a_scale,
+                                     const void *B, int64_t ldb, const float *b_scale,
+                                     void *Y, int64_t ldy,
+                                     void *workspace, size_t workspace_bytes, void *stream,
+                                     const qlin_config *cfg);
+
+/* Test hook: the raw int32 dot products acc[M][ldacc] = A * B^T of W8A8_INT8
+ * with the given config (NULL: the table's), no scaling, no rounding. */
+qlin_status qlin_int8_accumulate(int64_t M, int64_t N, int64_t K,
+                                 const void *A, int64_t lda, const void *B, int64_t ldb,
+                                 int32_t *acc, int64_t ldacc,
+                                 void *workspace, size_t workspace_bytes, void *stream,
+                                 const qlin_config *cfg);
+
+/* The config the table selects for a problem: the entry for (scaling, dt,
+ * N, K) at the smallest tuned M >= M (else the largest tuned M); shapes not
+ * in the table get the format's default for that M range. */
+qlin_status qlin_select_config(qlin_scaling sc, qlin_dtype dt, int64_t M, int64_t N,
+                               int64_t K, qlin_config *out);
+
+/* Workspace bytes needed by a config (NULL: the table's choice) for a
+ * problem; 0 when split_k == 1. */
+size_t qlin_workspace_size(qlin_scaling sc, qlin_dtype dt, int64_t M, int64_t N, int64_t K,
+                           const qlin_config *cfg);
+
+/* Validate a config for a problem without launching (QLIN_OK if it would run). */
+qlin_status qlin_check_config(qlin_scaling sc, qlin_dtype dt, int64_t M, int64_t N,
+                              int64_t K, const qlin_config *cfg);
+
+/* Enumerate the built kernel instances: fills *out with instance i (split_k
+ * and reduce set to 1 and 0) and returns QLIN_OK, or QLIN_ERR_BAD_ARGUMENT
+ * past the end.  *fmt_mask gets bit0 = e4m3 token/channel, bit1 = int8,
+ * bit2 = block. */
+qlin_status qlin_kernel_instance(int32_t i, qlin_config *out, int32_t *fmt_mask);
+
+/* Replace the config table with the text file at `path` (NULL or "" restores
+ * the compiled-in table).  Format: one entry per line,
+ *   <fmt> <N> <K> <M> <kernel> <variant> <tile_m> <tile_n> <tile_k>
+ *   <waves_n> <waves_k> <stages> <split_k> <reduce>
+ * with <fmt> one of fp8, int8, block_fp8; '#' starts a comment.  On error
+ * the previous table is kept. */
+qlin_status qlin_load_config_table(const char *path);
+
+/* Number of entries in the active table. */
+int32_t qlin_config_table_size(void);
+
+const char *qlin_status_string(qlin_status s);
+int32_t qlin_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLINEAR_H */

@@ -1,0 +1,324 @@
+"""int8_gemm_linear_amd -- MI355X (gfx950) quantized linear-layer GEMM.
+
+Thin Python binding over the C ABI of ``libqlinear.so`` (``include/qlinear.h``):
+argument marshalling only.  Every step of the computation runs in the HIP
+kernels of the library; there is no CPU or PyTorch fallback, and importing
+this package fails loudly when the library has not been built
+(``python -m int8_gemm_linear_amd.build``).  PyTorch supplies device memory
+and the current stream.
+
+    Y = scaled_mm(a_q, a_scale, b_q, b_scale)          # FP8_Dynamic / W8A8_INT8
+    Y = block_scaled_mm(a_q, a_scale, b_q, b_scale)    # Block_FP8
+
+``a_q`` [M,K] and ``b_q`` [N,K] (torch.float8_e4m3fn or torch.int8, rows
+K-contiguous); fp32 scales ``a_scale`` [M] and ``b_scale`` [N], or for the
+block format ``a_scale`` [M, K/128] and ``b_scale`` [N/128, K/128]; the
+result is bfloat16 [M,N].  Formats per "Building a High-Performance and
+Portable vLLM Linear Backend with Helion", section "Helion Linear Backend /
+Scope".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import asdict, dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlinear.so")
+
+E4M3, INT8 = 0, 1
+TOKEN_CHANNEL, BLOCK128 = 0, 1
+KERNEL_STREAM, KERNEL_TILE = 0, 1
+STANDARD, SWAP_AB = 0, 1
+REDUCE_TWO_PASS, REDUCE_LAST_ARRIVER = 0, 1
+
+_STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "bad leading dimension",
+           4: "misaligned pointer", 5: "workspace", 6: "bad config", 7: "config file",
+           8: "HIP launch failed", 9: "bad argument"}
+
+
+class QlinError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_lib().qlin_status_string(status).decode()} (status {status})")
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "kernel", "variant", "tile_m", "tile_n", "tile_k", "waves_n", "waves_k",
+        "stages", "split_k", "reduce")]
+
+
+@dataclass(frozen=True)
+class Config:
+    """One launch configuration (mirrors ``qlin_config``)."""
+    kernel: int
+    variant: int
+    tile_m: int
+    tile_n: int
+    tile_k: int
+    waves_n: int
+    waves_k: int
+    stages: int
+    split_k: int = 1
+    reduce: int = REDUCE_LAST_ARRIVER
+
+    def _c(self) -> _Cfg:
+        return _Cfg(**asdict(self))
+
+    @staticmethod
+    def _from_c(c: _Cfg) -> "Config":
+        return Config(**{f: getattr(c, f) for f, _ in _Cfg._fields_})
+
+    def replace(self, **kw) -> "Config":
+        d = asdict(self)
+        d.update(kw)
+        return Config(**d)
+
+
+_LIB = None
+
+
+def _check_single_hip_runtime():
+    # torch ships its own libamdhip64; the library must bind to that same
+    # runtime (it does: both carry the soname libamdhip64.so.7 and torch is
+    # loaded first).  Two runtimes in one process would not share streams.
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {ln.split()[-1] for ln in f if "libamdhip64" in ln}
+    except OSError:
+        return
+    if len(paths) > 1:
+        raise ImportError("two HIP runtimes are mapped into this process: " + ", ".join(sorted(paths)))
+
+
+def _lib():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m int8_gemm_linear_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    _check_single_hip_runtime()
+    P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    I = ctypes.c_int
+    CP = ctypes.POINTER(_Cfg)
+    lib.qlin_scaled_mm_cfg.argtypes = [I, I64, I64, I64, P, I64, P, P, I64, P, P, I64, P, SZ, P, CP]
+    lib.qlin_scaled_mm_cfg.restype = I
+    lib.qlin_scaled_mm.argtypes = [I, I64, I64, I64, P, I64, P, P, I64, P, P, I64, P, SZ, P]
+    lib.qlin_scaled_mm.restype = I
+    lib.qlin_block_scaled_mm_cfg.argtypes = [I64, I64, I64, P, I64, P, P, I64, P, P, I64, P, SZ, P, CP]
+    lib.qlin_block_scaled_mm_cfg.restype = I
+    lib.qlin_block_scaled_mm.argtypes = [I64, I64, I64, P, I64, P, P, I64, P, P, I64, P, SZ, P]
+    lib.qlin_block_scaled_mm.restype = I
+    lib.qlin_int8_accumulate.argtypes = [I64, I64, I64, P, I64, P, I64, P, I64, P, SZ, P, CP]
+    lib.qlin_int8_accumulate.restype = I
+    lib.qlin_select_config.argtypes = [I, I, I64, I64, I64, CP]
+    lib.qlin_select_config.restype = I
+    lib.qlin_check_config.argtypes = [I, I, I64, I64, I64, CP]
+    lib.qlin_check_config.restype = I
+    lib.qlin_workspace_size.argtypes = [I, I, I64, I64, I64, CP]
+    lib.qlin_workspace_size.restype = SZ
+    lib.qlin_kernel_instance.argtypes = [ctypes.c_int32, CP, ctypes.POINTER(ctypes.c_int32)]
+    lib.qlin_kernel_instance.restype = I
+    lib.qlin_load_config_table.argtypes = [ctypes.c_char_p]
+    lib.qlin_load_config_table.restype = I
+    lib.qlin_config_table_size.argtypes = []
+    lib.qlin_config_table_size.restype = ctypes.c_int32
+    lib.qlin_status_string.argtypes = [I]
+    lib.qlin_status_string.restype = ctypes.c_char_p
+    lib.qlin_abi_version.argtypes = []
+    lib.qlin_abi_version.restype = ctypes.c_int32
+    _LIB = lib
+    return lib
+
+
+def lib():
+    """The loaded ctypes handle of libqlinear.so."""
+    return _lib()
+
+
+# ---------------------------------------------------------------------------
+# Workspace: one zeroed device buffer per (device, stream), grown on demand.
+# The split-K counters in it are left zeroed by every call.
+# ---------------------------------------------------------------------------
+_WS: dict = {}
+
+
+def workspace_for(nbytes: int, device: torch.device, stream) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    key = (device.index, int(stream.cuda_stream))
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _WS[key] = buf
+    return buf
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float8_e4m3fn:
+        return E4M3
+    if t.dtype == torch.int8:
+        return INT8
+    raise TypeError(f"operands must be float8_e4m3fn or int8, got {t.dtype}")
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.stride(0)
+
+
+def _scale(t: torch.Tensor, shape, name: str) -> torch.Tensor:
+    if t.dtype != torch.float32 or not t.is_cuda:
+        raise ValueError(f"{name} must be a float32 device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _call(fn, args, what):
+    st = fn(*args)
+    if st != 0:
+        raise QlinError(st, what)
+
+
+def scaled_mm(a_q, a_scale, b_q, b_scale, out=None, config: Config | None = None, workspace=None):
+    """FP8_Dynamic (e4m3) or W8A8_INT8 (int8): bf16 [M,N] = sA[m] sB[n] (A B^T)."""
+    dt = _dt(a_q)
+    if b_q.dtype != a_q.dtype:
+        raise TypeError("A and B must have the same dtype")
+    lda, ldb = _rows(a_q, "a_q"), _rows(b_q, "b_q")
+    M, K = a_q.shape
+    N = b_q.shape[0]
+    if b_q.shape[1] != K:
+        raise ValueError("A is [M,K] and B must be [N,K]")
+    _scale(a_scale, (M,), "a_scale")
+    _scale(b_scale, (N,), "b_scale")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
+    elif out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1 or tuple(out.shape) != (M, N):
+        raise ValueError("out must be a bf16 [M,N] tensor with contiguous rows")
+    stream = torch.cuda.current_stream(a_q.device)
+    c = config._c() if config is not None else None
+    wsz = _lib().qlin_workspace_size(TOKEN_CHANNEL, dt, M, N, K, ctypes.byref(c) if c else None)
+    ws = workspace if workspace is not None else workspace_for(wsz, a_q.device, stream)
+    args = [dt, M, N, K, a_q.data_ptr(), lda, a_scale.data_ptr(), b_q.data_ptr(), ldb,
+            b_scale.data_ptr(), out.data_ptr(), out.stride(0),
+            ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+            stream.cuda_stream]
+    if c is None:
+        _call(_lib().qlin_scaled_mm, args, "qlin_scaled_mm")
+    else:
+        _call(_lib().qlin_scaled_mm_cfg, args + [ctypes.byref(c)], "qlin_scaled_mm_cfg")
+    return out
+
+
+def block_scaled_mm(a_q, a_scale, b_q, b_scale, out=None, config: Config | None = None,
+                    workspace=None):
+    """Block_FP8: bf16 [M,N] = sum_g sA[m,g] sB[n/128,g] (A B^T over group g)."""
+    if a_q.dtype != torch.float8_e4m3fn or b_q.dtype != torch.float8_e4m3fn:
+        raise TypeError("block_scaled_mm takes float8_e4m3fn operands")
+    lda, ldb = _rows(a_q, "a_q"), _rows(b_q, "b_q")
+    M, K = a_q.shape
+    N = b_q.shape[0]
+    if b_q.shape[1] != K:
+        raise ValueError("A is [M,K] and B must be [N,K]")
+    G = K // 128
+    _scale(a_scale, (M, G), "a_scale")
+    _scale(b_scale, (N // 128, G), "b_scale")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
+    elif out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1 or tuple(out.shape) != (M, N):
+        raise ValueError("out must be a bf16 [M,N] tensor with contiguous rows")
+    stream = torch.cuda.current_stream(a_q.device)
+    c = config._c() if config is not None else None
+    wsz = _lib().qlin_workspace_size(BLOCK128, E4M3, M, N, K, ctypes.byref(c) if c else None)
+    ws = workspace if workspace is not None else workspace_for(wsz, a_q.device, stream)
+    args = [M, N, K, a_q.data_ptr(), lda, a_scale.data_ptr(), b_q.data_ptr(), ldb,
+            b_scale.data_ptr(), out.data_ptr(), out.stride(0),
+            ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+            stream.cuda_stream]
+    if c is None:
+        _call(_lib().qlin_block_scaled_mm, args, "qlin_block_scaled_mm")
+    else:
+        _call(_lib().qlin_block_scaled_mm_cfg, args + [ctypes.byref(c)], "qlin_block_scaled_mm_cfg")
+    return out
+
+
+def int8_accumulate(a_q, b_q, config: Config | None = None, out=None):
+    """Test hook: raw int32 A B^T of int8 operands (no scaling, no rounding)."""
+    if a_q.dtype != torch.int8 or b_q.dtype != torch.int8:
+        raise TypeError("int8_accumulate takes int8 operands")
+    lda, ldb = _rows(a_q, "a_q"), _rows(b_q, "b_q")
+    M, K = a_q.shape
+    N = b_q.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.int32, device=a_q.device)
+    stream = torch.cuda.current_stream(a_q.device)
+    c = config._c() if config is not None else None
+    wsz = _lib().qlin_workspace_size(TOKEN_CHANNEL, INT8, M, N, K, ctypes.byref(c) if c else None)
+    ws = workspace_for(wsz, a_q.device, stream)
+    _call(_lib().qlin_int8_accumulate,
+          [M, N, K, a_q.data_ptr(), lda, b_q.data_ptr(), ldb, out.data_ptr(), out.stride(0),
+           ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+           stream.cuda_stream, ctypes.byref(c) if c else None], "qlin_int8_accumulate")
+    return out
+
+
+FORMATS = {"fp8": (TOKEN_CHANNEL, E4M3), "int8": (TOKEN_CHANNEL, INT8), "block_fp8": (BLOCK128, E4M3)}
+
+
+def select_config(fmt: str, M: int, N: int, K: int) -> Config:
+    sc, dt = FORMATS[fmt]
+    c = _Cfg()
+    _call(_lib().qlin_select_config, [sc, dt, M, N, K, ctypes.byref(c)], "qlin_select_config")
+    return Config._from_c(c)
+
+
+def check_config(fmt: str, M: int, N: int, K: int, config: Config) -> int:
+    sc, dt = FORMATS[fmt]
+    c = config._c()
+    return _lib().qlin_check_config(sc, dt, M, N, K, ctypes.byref(c))
+
+
+def workspace_size(fmt: str, M: int, N: int, K: int, config: Config | None = None) -> int:
+    sc, dt = FORMATS[fmt]
+    c = config._c() if config is not None else None
+    return _lib().qlin_workspace_size(sc, dt, M, N, K, ctypes.byref(c) if c else None)
+
+
+def kernel_instances():
+    """[(Config, fmt_mask)] of every built kernel instance (bit0 fp8, bit1 int8, bit2 block)."""
+    out = []
+    i = 0
+    c = _Cfg()
+    m = ctypes.c_int32()
+    while _lib().qlin_kernel_instance(i, ctypes.byref(c), ctypes.byref(m)) == 0:
+        out.append((Config._from_c(c), m.value))
+        i += 1
+    return out
+
+
+def instances_for(fmt: str):
+    bit = {"fp8": 1, "int8": 2, "block_fp8": 4}[fmt]
+    return [c for c, m in kernel_instances() if m & bit]
+
+
+def load_config_table(path: str | None):
+    _call(_lib().qlin_load_config_table, [path.encode() if path else None], "qlin_load_config_table")
+
+
+def config_table_size() -> int:
+    return _lib().qlin_config_table_size()
+
+
+def abi_version() -> int:
+    return _lib().qlin_abi_version()

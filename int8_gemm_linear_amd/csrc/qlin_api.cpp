@@ -1,0 +1,558 @@
+// The C ABI of libqlinear.so: argument validation (host only, before any HIP
+// call), the per-shape config table, kernel-instance lookup and launch.
+//
+// Dispatch follows the approach of "Building a High-Performance and Portable
+// vLLM Linear Backend with Helion" ("Kernel Implementation" section): the
+// algorithm variant (Standard / Split-K / Swap-AB) and the low-level launch
+// configuration are data chosen per input shape by an offline sweep, not a
+// hand-written rule such as "Swap-AB below 32 tokens".  On the call path the
+// choice is a table lookup keyed by (format, N, K) and the token count M.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cctype>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <mutex>
+#include <sstream>
+#include <string>
+#include <vector>
+
+#include "qlin_internal.h"
+
+#include "qlin_config_table.inc"   // kDefaultTable: the tuned table as text
+
+using namespace qlin;
+
+namespace {
+
+const int64_t kMaxMN = int64_t(1) << 24;
+const int64_t kMaxK = int64_t(1) << 20;
+const int64_t kMaxKInt8 = (int64_t(1) << 17) - 16;   // |acc| <= K*128*128 < 2^31
+const int64_t kMaxLd = (int64_t(1) << 31) - 1;
+
+// Workspace layout: [counters: kCounterBytes][split partials].  The counter
+// region sits at a fixed place for every config, so partials written by one
+// config never land on the counters another config relies on being zero.
+const size_t kCounterBytes = 128 * 1024;
+const int64_t kMaxCounters = (int64_t)(kCounterBytes / 4);
+
+int fmt_bit(int fmt, int scal)
+{
+    if (scal == SC_BLOCK)
+        return FB_BLOCK;
+    return fmt == FMT_INT8 ? FB_INT8 : FB_FP8;
+}
+
+const std::vector<Instance> &registry()
+{
+    static const std::vector<Instance> all = [] {
+        std::vector<Instance> r;
+        const Instance *(*fns[])(int *) = {
+            stream_instances_fp8, stream_instances_int8, stream_instances_block,
+            tile_instances_fp8, tile_instances_int8, tile_instances_block,
+        };
+        for (auto f : fns) {
+            int n = 0;
+            const Instance *p = f(&n);
+            r.insert(r.end(), p, p + n);
+        }
+        return r;
+    }();
+    return all;
+}
+
+bool same_shape(const qlin_config &a, const qlin_config &b)
+{
+    return a.kernel == b.kernel && a.variant == b.variant && a.tile_m == b.tile_m &&
+           a.tile_n == b.tile_n && a.tile_k == b.tile_k && a.waves_n == b.waves_n &&
+           a.waves_k == b.waves_k && a.stages == b.stages;
+}
+
+const Instance *find_instance(int fmt, int scal, const qlin_config &c)
+{
+    const int bit = fmt_bit(fmt, scal);
+    for (const Instance &in : registry())
+        if ((in.fmt_mask & bit) && same_shape(in.cfg, c))
+            return &in;
+    return nullptr;
+}
+
+// ---------------------------------------------------------------------------
+// Config table
+// ---------------------------------------------------------------------------
+struct Entry {
+    int bit;
+    int64_t N, K, M;
+    qlin_config cfg;
+};
+
+std::vector<Entry> g_table;
+bool g_table_ready = false;
+std::mutex g_table_mutex;
+int g_log = -1;
+
+bool parse_table(const std::string &text, std::vector<Entry> &out)
+{
+    std::istringstream in(text);
+    std::string line;
+    std::vector<Entry> t;
+    while (std::getline(in, line)) {
+        const size_t h = line.find('#');
+        if (h != std::string::npos)
+            line.resize(h);
+        std::istringstream ls(line);
+        std::string fmt;
+        if (!(ls >> fmt))
+            continue;  // blank or comment
+        Entry e;
+        if (fmt == "fp8")
+            e.bit = FB_FP8;
+        else if (fmt == "int8")
+            e.bit = FB_INT8;
+        else if (fmt == "block_fp8")
+            e.bit = FB_BLOCK;
+        else
+            return false;
+        qlin_config &c = e.cfg;
+        if (!(ls >> e.N >> e.K >> e.M >> c.kernel >> c.variant >> c.tile_m >> c.tile_n >> c.tile_k >>
+              c.waves_n >> c.waves_k >> c.stages >> c.split_k >> c.reduce))
+            return false;
+        std::string extra;
+        if (ls >> extra)
+            return false;
+        if (e.N <= 0 || e.K <= 0 || e.M <= 0)
+            return false;
+        t.push_back(e);
+    }
+    out.swap(t);
+    return true;
+}
+
+void ensure_table()
+{
+    if (g_table_ready)
+        return;
+    std::lock_guard<std::mutex> lk(g_table_mutex);
+    if (g_table_ready)
+        return;
+    if (g_log < 0) {
+        const char *e = std::getenv("QLIN_LOG");
+        g_log = (e && *e && *e != '0') ? 1 : 0;
+    }
+    std::vector<Entry> t;
+    bool ok = false;
+    const char *path = std::getenv("QLIN_CONFIG");
+    if (path && *path) {
+        std::ifstream f(path);
+        if (f) {
+            std::stringstream ss;
+            ss << f.rdbuf();
+            ok = parse_table(ss.str(), t);
+        }
+    }
+    if (!ok)
+        parse_table(kDefaultTable, t);
+    g_table.swap(t);
+    g_table_ready = true;
+}
+
+int ilog2_exact(int v)
+{
+    if (v <= 0 || (v & (v - 1)))
+        return -1;
+    int l = 0;
+    while ((1 << l) < v)
+        ++l;
+    return l;
+}
+
+// Stream kernel: grid (weight tiles, token tiles); tile kernel: one flat
+// dimension over all output tiles (remapped in-kernel for XCD locality).
+void grid_of(const qlin_config &c, int64_t M, int64_t N, int64_t *gx, int64_t *gy)
+{
+    const int64_t tn = (N + c.tile_n - 1) / c.tile_n;
+    const int64_t tm = (M + c.tile_m - 1) / c.tile_m;
+    if (c.kernel == QLIN_KERNEL_TILE) {
+        *gx = tn * tm;
+        *gy = 1;
+    } else {
+        *gx = tn;
+        *gy = tm;
+    }
+}
+
+// Built-in choice for shapes the table does not cover.
+qlin_config default_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
+{
+    qlin_config c;
+    std::memset(&c, 0, sizeof c);
+    const int64_t KS = (K + 127) / 128;
+    bool have_tile = false;
+    for (const Instance &in : registry())
+        if (in.cfg.kernel == QLIN_KERNEL_TILE && (in.fmt_mask & fmt_bit(fmt, scal)))
+            have_tile = true;
+    if (M > 64 && have_tile && K % 128 == 0) {
+        c.kernel = QLIN_KERNEL_TILE;
+        c.variant = QLIN_SWAP_AB;          // built for all three formats
+        c.tile_m = 128;
+        c.tile_n = 128;
+        c.tile_k = 128;
+        c.waves_n = 2;
+        c.waves_k = 2;
+        c.stages = 2;
+    } else {
+        c.kernel = QLIN_KERNEL_STREAM;
+        c.variant = QLIN_SWAP_AB;
+        c.tile_m = M <= 16 ? 16 : 32;
+        c.tile_n = 64;
+        c.tile_k = 256;
+        c.waves_n = 2;
+        c.waves_k = 2;
+        c.stages = 2;
+    }
+    int64_t gx, gy;
+    grid_of(c, M, N, &gx, &gy);
+    const int64_t kw = c.kernel == QLIN_KERNEL_STREAM ? c.waves_k : 1;
+    int split = 1;
+    while (gx * gy * split < 512 && split * 2 <= 256 && split * 2 * kw <= KS)
+        split *= 2;
+    c.split_k = split;
+    c.reduce = gx * gy <= kMaxCounters ? QLIN_REDUCE_LAST_ARRIVER : QLIN_REDUCE_TWO_PASS;
+    return c;
+}
+
+qlin_config select_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
+{
+    ensure_table();
+    const int bit = fmt_bit(fmt, scal);
+    const Entry *best = nullptr, *largest = nullptr;
+    for (const Entry &e : g_table) {
+        if (e.bit != bit || e.N != N || e.K != K)
+            continue;
+        if (e.M >= M && (!best || e.M < best->M))
+            best = &e;
+        if (!largest || e.M > largest->M)
+            largest = &e;
+    }
+    if (!best)
+        best = largest;
+    if (best)
+        return best->cfg;
+    return default_config(fmt, scal, M, N, K);
+}
+
+qlin_status check_config(int fmt, int scal, int64_t M, int64_t N, int64_t K,
+                         const qlin_config &c, const Instance **inst)
+{
+    const Instance *in = find_instance(fmt, scal, c);
+    if (!in)
+        return QLIN_ERR_BAD_CONFIG;
+    const int64_t KS = (K + 127) / 128;
+    if (ilog2_exact(c.split_k) < 0 || c.split_k > 256 || c.split_k > KS)
+        return QLIN_ERR_BAD_CONFIG;
+    if (c.reduce != QLIN_REDUCE_TWO_PASS && c.reduce != QLIN_REDUCE_LAST_ARRIVER)
+        return QLIN_ERR_BAD_CONFIG;
+    if (c.kernel == QLIN_KERNEL_TILE && K % 128 != 0)
+        return QLIN_ERR_BAD_CONFIG;   // the LDS ring copies whole 128-byte K steps
+    int64_t gx, gy;
+    grid_of(c, M, N, &gx, &gy);
+    if (gx > 0x7fffffff || gy > 65535)
+        return QLIN_ERR_BAD_CONFIG;
+    if (c.split_k > 1 && c.reduce == QLIN_REDUCE_LAST_ARRIVER && gx * gy > kMaxCounters)
+        return QLIN_ERR_BAD_CONFIG;   // one counter per output tile must fit its region
+    if (inst)
+        *inst = in;
+    return QLIN_OK;
+}
+
+size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+size_t ws_bytes(const qlin_config &c, int64_t M, int64_t N)
+{
+    if (c.split_k <= 1 || M == 0 || N == 0)
+        return 0;
+    return kCounterBytes + round256((size_t)c.split_k * (size_t)M * (size_t)N * 4);
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+qlin_status validate(const Problem &pb)
+{
+    if (pb.fmt != FMT_E4M3 && pb.fmt != FMT_INT8)
+        return QLIN_ERR_BAD_ARGUMENT;
+    if (pb.scal == SC_BLOCK && pb.fmt != FMT_E4M3)
+        return QLIN_ERR_BAD_ARGUMENT;
+    if (pb.M < 0 || pb.N < 0 || pb.M > kMaxMN || pb.N > kMaxMN)
+        return QLIN_ERR_BAD_SHAPE;
+    if (pb.K <= 0 || pb.K % 16 != 0 || pb.K > kMaxK)
+        return QLIN_ERR_BAD_SHAPE;
+    if (pb.fmt == FMT_INT8 && pb.K > kMaxKInt8)
+        return QLIN_ERR_BAD_SHAPE;
+    if (pb.scal == SC_BLOCK && (pb.K % 128 != 0 || pb.N % 128 != 0))
+        return QLIN_ERR_BAD_SHAPE;
+    if (pb.M == 0 || pb.N == 0)
+        return QLIN_OK;
+    const bool raw = pb.acc_out != nullptr;
+    if (!pb.A || !pb.B || (!raw && (!pb.sA || !pb.sB || !pb.Y)))
+        return QLIN_ERR_NULL_POINTER;
+    if (pb.lda < pb.K || pb.ldb < pb.K || pb.lda % 16 || pb.ldb % 16 || pb.lda > kMaxLd ||
+        pb.ldb > kMaxLd)
+        return QLIN_ERR_BAD_STRIDE;
+    if (raw ? (pb.ldacc < pb.N || pb.ldacc > kMaxLd) : (pb.ldy < pb.N || pb.ldy > kMaxLd))
+        return QLIN_ERR_BAD_STRIDE;
+    if (!aligned(pb.A, 16) || !aligned(pb.B, 16))
+        return QLIN_ERR_MISALIGNED;
+    if (raw ? !aligned(pb.acc_out, 16)
+            : (!aligned(pb.Y, 16) || !aligned(pb.sA, 4) || !aligned(pb.sB, 4)))
+        return QLIN_ERR_MISALIGNED;
+    return QLIN_OK;
+}
+
+qlin_status run(const Problem &pb, const qlin_config *cfg_in)
+{
+    qlin_status st = validate(pb);
+    if (st != QLIN_OK)
+        return st;
+    if (pb.M == 0 || pb.N == 0)
+        return cfg_in ? (find_instance(pb.fmt, pb.scal, *cfg_in) ? QLIN_OK : QLIN_ERR_BAD_CONFIG)
+                      : QLIN_OK;
+    const qlin_config cfg = cfg_in ? *cfg_in : select_config(pb.fmt, pb.scal, pb.M, pb.N, pb.K);
+    const Instance *inst = nullptr;
+    st = check_config(pb.fmt, pb.scal, pb.M, pb.N, pb.K, cfg, &inst);
+    if (st != QLIN_OK)
+        return st;
+    const size_t need = ws_bytes(cfg, pb.M, pb.N);
+    if (need) {
+        if (!pb.ws || pb.ws_bytes < need)
+            return QLIN_ERR_WORKSPACE;
+        if (!aligned(pb.ws, 16))
+            return QLIN_ERR_MISALIGNED;
+    }
+    if (g_log > 0)
+        std::fprintf(stderr,
+                     "[qlinear] fmt=%d scal=%d M=%lld N=%lld K=%lld -> kernel=%d variant=%d "
+                     "tile=%dx%dx%d waves=%dx%d stages=%d split_k=%d reduce=%d\n",
+                     pb.fmt, pb.scal, (long long)pb.M, (long long)pb.N, (long long)pb.K, cfg.kernel,
+                     cfg.variant, cfg.tile_m, cfg.tile_n, cfg.tile_k, cfg.waves_n, cfg.waves_k,
+                     cfg.stages, cfg.split_k, cfg.reduce);
+
+    KArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.A = static_cast<const uint8_t *>(pb.A);
+    a.B = static_cast<const uint8_t *>(pb.B);
+    a.sA = pb.sA;
+    a.sB = pb.sB;
+    a.Y = static_cast<uint16_t *>(pb.Y);
+    a.acc_out = pb.acc_out;
+    a.M = (int)pb.M;
+    a.N = (int)pb.N;
+    a.K = (int)pb.K;
+    a.lda = (int)pb.lda;
+    a.ldb = (int)pb.ldb;
+    a.ldy = (int)pb.ldy;
+    a.ldacc = (int)pb.ldacc;
+    a.G = (int)(pb.K / 128);
+    a.split_k = cfg.split_k;
+    const int64_t KS = (pb.K + 127) / 128;
+    a.steps_per_split = (int)((KS + cfg.split_k - 1) / cfg.split_k);
+    a.reduce = cfg.reduce;
+    if (cfg.split_k > 1) {
+        a.counters = static_cast<int32_t *>(pb.ws);
+        a.part = static_cast<char *>(pb.ws) + kCounterBytes;
+    }
+    int64_t gx, gy;
+    grid_of(cfg, pb.M, pb.N, &gx, &gy);
+    const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)cfg.split_k);
+    hipError_t e = inst->fn(a, grid, pb.stream);
+    if (e == hipSuccess && cfg.split_k > 1 && cfg.reduce == QLIN_REDUCE_TWO_PASS)
+        e = launch_reduce(pb.fmt, pb.scal, a, pb.stream);
+    return e == hipSuccess ? QLIN_OK : QLIN_ERR_HIP;
+}
+
+Problem make_problem(int fmt, int scal, int64_t M, int64_t N, int64_t K, const void *A,
+                     int64_t lda, const float *sA, const void *B, int64_t ldb, const float *sB,
+                     void *Y, int64_t ldy, void *ws, size_t wsb, void *stream)
+{
+    Problem pb;
+    std::memset(&pb, 0, sizeof pb);
+    pb.fmt = fmt;
+    pb.scal = scal;
+    pb.M = M;
+    pb.N = N;
+    pb.K = K;
+    pb.A = A;
+    pb.lda = lda;
+    pb.sA = sA;
+    pb.B = B;
+    pb.ldb = ldb;
+    pb.sB = sB;
+    pb.Y = Y;
+    pb.ldy = ldy;
+    pb.ws = ws;
+    pb.ws_bytes = wsb;
+    pb.stream = static_cast<hipStream_t>(stream);
+    return pb;
+}
+
+int fmt_of(qlin_dtype dt) { return dt == QLIN_INT8 ? FMT_INT8 : (dt == QLIN_E4M3 ? FMT_E4M3 : -1); }
+
+}  // namespace
+
+extern "C" {
+
+qlin_status qlin_scaled_mm_cfg(qlin_dtype dt, int64_t M, int64_t N, int64_t K, const void *A,
+                               int64_t lda, const float *a_scale, const void *B, int64_t ldb,
+                               const float *b_scale, void *Y, int64_t ldy, void *workspace,
+                               size_t workspace_bytes, void *stream, const qlin_config *cfg)
+{
+    const int fmt = fmt_of(dt);
+    if (fmt < 0)
+        return QLIN_ERR_BAD_ARGUMENT;
+    return run(make_problem(fmt, SC_TC, M, N, K, A, lda, a_scale, B, ldb, b_scale, Y, ldy,
+                            workspace, workspace_bytes, stream),
+               cfg);
+}
+
+qlin_status qlin_scaled_mm(qlin_dtype dt, int64_t M, int64_t N, int64_t K, const void *A,
+                           int64_t lda, const float *a_scale, const void *B, int64_t ldb,
+                           const float *b_scale, void *Y, int64_t ldy, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    return qlin_scaled_mm_cfg(dt, M, N, K, A, lda, a_scale, B, ldb, b_scale, Y, ldy, workspace,
+                              workspace_bytes, stream, nullptr);
+}
+
+qlin_status qlin_block_scaled_mm_cfg(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                                     const float *a_scale, const void *B, int64_t ldb,
+                                     const float *b_scale, void *Y, int64_t ldy, void *workspace,
+                                     size_t workspace_bytes, void *stream, const qlin_config *cfg)
+{
+    return run(make_problem(FMT_E4M3, SC_BLOCK, M, N, K, A, lda, a_scale, B, ldb, b_scale, Y, ldy,
+                            workspace, workspace_bytes, stream),
+               cfg);
+}
+
+qlin_status qlin_block_scaled_mm(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                                 const float *a_scale, const void *B, int64_t ldb,
+                                 const float *b_scale, void *Y, int64_t ldy, void *workspace,
+                                 size_t workspace_bytes, void *stream)
+{
+    return qlin_block_scaled_mm_cfg(M, N, K, A, lda, a_scale, B, ldb, b_scale, Y, ldy, workspace,
+                                    workspace_bytes, stream, nullptr);
+}
+
+qlin_status qlin_int8_accumulate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                                 const void *B, int64_t ldb, int32_t *acc, int64_t ldacc,
+                                 void *workspace, size_t workspace_bytes, void *stream,
+                                 const qlin_config *cfg)
+{
+    Problem pb = make_problem(FMT_INT8, SC_TC, M, N, K, A, lda, nullptr, B, ldb, nullptr, nullptr,
+                              0, workspace, workspace_bytes, stream);
+    pb.acc_out = acc;
+    pb.ldacc = ldacc;
+    if (!acc && M > 0 && N > 0)
+        return QLIN_ERR_NULL_POINTER;
+    return run(pb, cfg);
+}
+
+qlin_status qlin_select_config(qlin_scaling sc, qlin_dtype dt, int64_t M, int64_t N, int64_t K,
+                               qlin_config *out)
+{
+    const int fmt = fmt_of(dt);
+    if (fmt < 0 || (sc != QLIN_TOKEN_CHANNEL && sc != QLIN_BLOCK128) ||
+        (sc == QLIN_BLOCK128 && fmt != FMT_E4M3))
+        return QLIN_ERR_BAD_ARGUMENT;
+    if (!out)
+        return QLIN_ERR_NULL_POINTER;
+    if (M < 0 || N < 0 || K <= 0)
+        return QLIN_ERR_BAD_SHAPE;
+    *out = select_config(fmt, sc == QLIN_BLOCK128 ? SC_BLOCK : SC_TC, M, N, K);
+    return QLIN_OK;
+}
+
+qlin_status qlin_check_config(qlin_scaling sc, qlin_dtype dt, int64_t M, int64_t N, int64_t K,
+                              const qlin_config *cfg)
+{
+    const int fmt = fmt_of(dt);
+    if (fmt < 0 || (sc != QLIN_TOKEN_CHANNEL && sc != QLIN_BLOCK128) ||
+        (sc == QLIN_BLOCK128 && fmt != FMT_E4M3))
+        return QLIN_ERR_BAD_ARGUMENT;
+    if (!cfg)
+        return QLIN_ERR_NULL_POINTER;
+    if (M < 0 || N < 0 || K <= 0 || K % 16)
+        return QLIN_ERR_BAD_SHAPE;
+    return check_config(fmt, sc == QLIN_BLOCK128 ? SC_BLOCK : SC_TC, M, N, K, *cfg, nullptr);
+}
+
+size_t qlin_workspace_size(qlin_scaling sc, qlin_dtype dt, int64_t M, int64_t N, int64_t K,
+                           const qlin_config *cfg)
+{
+    const int fmt = fmt_of(dt);
+    if (fmt < 0 || M <= 0 || N <= 0 || K <= 0)
+        return 0;
+    const int scal = sc == QLIN_BLOCK128 ? SC_BLOCK : SC_TC;
+    const qlin_config c = cfg ? *cfg : select_config(fmt, scal, M, N, K);
+    return ws_bytes(c, M, N);
+}
+
+qlin_status qlin_kernel_instance(int32_t i, qlin_config *out, int32_t *fmt_mask)
+{
+    const std::vector<Instance> &r = registry();
+    if (i < 0 || (size_t)i >= r.size())
+        return QLIN_ERR_BAD_ARGUMENT;
+    if (!out || !fmt_mask)
+        return QLIN_ERR_NULL_POINTER;
+    *out = r[i].cfg;
+    *fmt_mask = r[i].fmt_mask;
+    return QLIN_OK;
+}
+
+qlin_status qlin_load_config_table(const char *path)
+{
+    std::vector<Entry> t;
+    if (!path || !*path) {
+        parse_table(kDefaultTable, t);
+    } else {
+        std::ifstream f(path);
+        if (!f)
+            return QLIN_ERR_CONFIG_FILE;
+        std::stringstream ss;
+        ss << f.rdbuf();
+        if (!parse_table(ss.str(), t))
+            return QLIN_ERR_CONFIG_FILE;
+    }
+    ensure_table();
+    std::lock_guard<std::mutex> lk(g_table_mutex);
+    g_table.swap(t);
+    return QLIN_OK;
+}
+
+int32_t qlin_config_table_size(void)
+{
+    ensure_table();
+    return (int32_t)g_table.size();
+}
+
+const char *qlin_status_string(qlin_status s)
+{
+    switch (s) {
+    case QLIN_OK: return "ok";
+    case QLIN_ERR_NULL_POINTER: return "null pointer";
+    case QLIN_ERR_BAD_SHAPE: return "bad shape";
+    case QLIN_ERR_BAD_STRIDE: return "bad leading dimension";
+    case QLIN_ERR_MISALIGNED: return "misaligned pointer";
+    case QLIN_ERR_WORKSPACE: return "workspace missing or too small";
+    case QLIN_ERR_BAD_CONFIG: return "invalid or unbuilt config";
+    case QLIN_ERR_CONFIG_FILE: return "config table file unreadable or malformed";
+    case QLIN_ERR_HIP: return "HIP launch failed";
+    case QLIN_ERR_BAD_ARGUMENT: return "bad argument";
+    }
+    return "unknown status";
+}
+
+int32_t qlin_abi_version(void) { return QLINEAR_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,178 @@
+// Device-side building blocks for the gfx950 kernels: matrix-core wrappers,
+// the 128-byte K step, bf16 rounding, and the scale-and-store epilogue.
+#pragma once
+
+#include <hip/hip_bf16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qlin_internal.h"
+
+namespace qlin {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Accumulator element: exact int32 for int8 operands, fp32 for e4m3.
+template <int FMT> struct AccT;
+template <> struct AccT<FMT_INT8> { typedef int32_t scalar; typedef v4i v4; typedef v16i v16; };
+template <> struct AccT<FMT_E4M3> { typedef float scalar; typedef v4f v4; typedef v16f v16; };
+
+__device__ inline v4i zero4i() { return v4i{0, 0, 0, 0}; }
+
+// One 128-byte K step of a 16x16 output block on the matrix cores.
+//
+// Operand layout (verified on gfx950 for both instructions): lane l feeds
+// row (l % 16) of its operand and holds 32 bytes of K, the bytes
+// [32*(l/16), 32*(l/16)+32) of the step, as x0 (first 16) and x1 (next 16).
+// The A-side and B-side operands use the same lane -> K mapping, so the
+// K sum is complete whatever slot order the hardware uses inside a lane.
+//   int8: two v_mfma_i32_16x16x64_i8 (x0 pair, then x1 pair), exact int32.
+//   e4m3: one v_mfma_f32_16x16x128_f8f6f4 (format 0 = OCP e4m3, no block
+//         scaling), fp32 accumulate.
+// Result layout: lane l holds column (l % 16), rows 4*(l/16) + 0..3.
+template <int FMT>
+__device__ inline typename AccT<FMT>::v4 mma16(v4i a0, v4i a1, v4i b0, v4i b1,
+                                               typename AccT<FMT>::v4 c);
+
+template <>
+__device__ inline v4i mma16<FMT_INT8>(v4i a0, v4i a1, v4i b0, v4i b1, v4i c)
+{
+    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, c, 0, 0, 0);
+    return c;
+}
+
+template <>
+__device__ inline v4f mma16<FMT_E4M3>(v4i a0, v4i a1, v4i b0, v4i b1, v4f c)
+{
+    v8i a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+    v8i b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+    // cbsz/blgp = 0: both operands e4m3; scale operands 0 select the
+    // unscaled encoding (no microscaling).
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// 32x32 blocks: lane l feeds row (l % 32) and holds 64 bytes of the 128-byte
+// K step, bytes [64*(l/32), 64*(l/32)+64), as x[0..3] (16 bytes each).
+//   int8: four v_mfma_i32_32x32x32_i8 (one per 16-byte piece).
+//   e4m3: two v_mfma_f32_32x32x64_f8f6f4 (pieces 0-1, then 2-3).
+// Result layout: lane l holds column (l % 32), rows 8*(v/4) + 4*(l/32) + v%4.
+template <int FMT>
+__device__ inline typename AccT<FMT>::v16 mma32(const v4i *a, const v4i *b,
+                                                typename AccT<FMT>::v16 c);
+
+template <>
+__device__ inline v16i mma32<FMT_INT8>(const v4i *a, const v4i *b, v16i c)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[j], b[j], c, 0, 0, 0);
+    return c;
+}
+
+template <>
+__device__ inline v16f mma32<FMT_E4M3>(const v4i *a, const v4i *b, v16f c)
+{
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        v8i x = __builtin_shufflevector(a[2 * j], a[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+        v8i y = __builtin_shufflevector(b[2 * j], b[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 0, 0, 0);
+    }
+    return c;
+}
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950;
+// NaN stays NaN, overflow goes to infinity, fp32 subnormals are kept).
+__device__ inline uint16_t bf16_bits(float f)
+{
+    __hip_bfloat16 h = __float2bfloat16(f);
+    return *reinterpret_cast<uint16_t *>(&h);
+}
+
+__device__ inline v4i ld_nt(const uint8_t *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+}
+
+__device__ inline v4i ld16(const uint8_t *p)
+{
+    return *reinterpret_cast<const v4i *>(p);
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue.  `v` is the full-K dot product for (t, n): an int32 (int8), an
+// fp32 sum (e4m3, token/channel), or the already group-scaled fp32 sum
+// (Block_FP8).  Token/channel scaling multiplies by sA[t] then sB[n] in fp32;
+// the result is rounded once to bf16.
+// ---------------------------------------------------------------------------
+template <int FMT, int SCAL>
+__device__ inline float finish_value(const KArgs &p, int t, int n,
+                                     typename AccT<FMT>::scalar v)
+{
+    if (SCAL == SC_BLOCK)
+        return (float)v;
+    return ((float)v * p.sA[t]) * p.sB[n];
+}
+
+// Store one final value.  Raw mode (acc_out != NULL) writes the int32 sum.
+template <int FMT, int SCAL>
+__device__ inline void store_final(const KArgs &p, int t, int n, typename AccT<FMT>::scalar v)
+{
+    if (FMT == FMT_INT8 && p.acc_out) {
+        p.acc_out[(int64_t)t * p.ldacc + n] = (int32_t)v;
+        return;
+    }
+    p.Y[(int64_t)t * p.ldy + n] = bf16_bits(finish_value<FMT, SCAL>(p, t, n, v));
+}
+
+// Store four final values for columns n..n+3 of row t (all in range).
+template <int FMT, int SCAL>
+__device__ inline void store_final4(const KArgs &p, int t, int n,
+                                    typename AccT<FMT>::v4 v)
+{
+    if (FMT == FMT_INT8 && p.acc_out) {
+        int32_t *d = p.acc_out + (int64_t)t * p.ldacc + n;
+        if ((p.ldacc & 3) == 0) {
+            *reinterpret_cast<v4i *>(d) = v4i{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) d[j] = (int32_t)v[j];
+        }
+        return;
+    }
+    uint16_t h[4];
+    if (SCAL == SC_BLOCK) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = bf16_bits((float)v[j]);
+    } else {
+        const float sa = p.sA[t];
+        const float *sb = p.sB + n;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = bf16_bits(((float)v[j] * sa) * sb[j]);
+    }
+    uint16_t *d = p.Y + (int64_t)t * p.ldy + n;
+    if ((p.ldy & 3) == 0) {
+        uint2 w;
+        w.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+        w.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+        *reinterpret_cast<uint2 *>(d) = w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[j] = h[j];
+    }
+}
+
+// Partials: [split][M][N], 4-byte elements, row stride N.
+template <int FMT>
+__device__ inline typename AccT<FMT>::scalar *part_ptr(const KArgs &p, int split, int t, int n)
+{
+    typedef typename AccT<FMT>::scalar S;
+    return reinterpret_cast<S *>(p.part) + ((int64_t)split * p.M + t) * p.N + n;
+}
+
+}  // namespace qlin

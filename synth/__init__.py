@@ -23,6 +23,7 @@ pages evaluate (Qwen3 1.7B / 8B / 32B class): activations ~ N(0,1), some with
 from __future__ import annotations
 
 from dataclasses import dataclass, field
+from functools import lru_cache
 
 import numpy as np
 
@@ -140,6 +141,24 @@ def quantize(fmt: str, x: np.ndarray, w: np.ndarray):
     return A, sA, B, sB
 
 
+@lru_cache(maxsize=4)
+def quantized_weight(fmt: str, N: int, K: int, root: int = 0):
+    """Codes and scales of the seeded weight [N,K] (shared by every M)."""
+    w = weights(N, K, (root, 1, K, N))
+    if fmt == "block_fp8":
+        B, sB = quant_blocks(w)
+    else:
+        B, sB = quant_rows(w, fmt)
+    return B, sB
+
+
+def quantized_activation(fmt: str, M: int, K: int, root: int = 0, outliers: bool = False):
+    x = activations(M, K, (root, 2, M, K), outliers=outliers, outlier_key=(root, 3, K))
+    if fmt == "block_fp8":
+        return quant_groups(x)
+    return quant_rows(x, fmt)
+
+
 def make_case(fmt: str, M: int, N: int, K: int, *, outliers: bool | None = None,
               root: int = 0, tag: str = "") -> Case:
     """The seeded recipe: B from SeedSequence([root,1,K,N]) (shared across M),
@@ -149,9 +168,8 @@ def make_case(fmt: str, M: int, N: int, K: int, *, outliers: bool | None = None,
         raise ValueError(fmt)
     if outliers is None:
         outliers = fmt != "int8"
-    w = weights(N, K, (root, 1, K, N))
-    x = activations(M, K, (root, 2, M, K), outliers=outliers, outlier_key=(root, 3, K))
-    A, sA, B, sB = quantize(fmt, x, w)
+    B, sB = quantized_weight(fmt, N, K, root)
+    A, sA = quantized_activation(fmt, M, K, root, outliers)
     return Case(fmt, M, N, K, A, sA, B, sB, tag=tag or f"{fmt}-M{M}-N{N}-K{K}")
 
 

@@ -1,0 +1,178 @@
+"""The C ABI on the host (no GPU needed): exported symbols, argument
+validation, config selection and the config-table parser.  Every call here
+fails validation or is a pure host query, so no kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int8_gemm_linear_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "qlinear.h")
+
+ST = {"ok": 0, "null": 1, "shape": 2, "stride": 3, "align": 4, "ws": 5, "cfg": 6, "file": 7,
+      "hip": 8, "arg": 9}
+A16 = 0x10000          # fake, 16-byte aligned device addresses (never dereferenced)
+B16 = 0x20000
+Y16 = 0x30000
+S4 = 0x40000
+
+
+def declared_functions():
+    text = open(HDR).read()
+    return sorted(set(re.findall(r"\b(qlin_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = q.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert q.abi_version() == 1
+
+
+def smm(dt=q.INT8, M=16, N=256, K=1024, A=A16, lda=None, sA=S4, B=B16, ldb=None, sB=S4,
+        Y=Y16, ldy=None, ws=None, wsb=0, cfg=None):
+    lib = q.lib()
+    args = [dt, M, N, K, A, K if lda is None else lda, sA, B, K if ldb is None else ldb, sB, Y,
+            N if ldy is None else ldy, ws, wsb, None]
+    if cfg is None:
+        return lib.qlin_scaled_mm(*args)
+    c = cfg._c()
+    return lib.qlin_scaled_mm_cfg(*args, ctypes.byref(c))
+
+
+def bmm(M=16, N=256, K=1024, **kw):
+    lib = q.lib()
+    return lib.qlin_block_scaled_mm(M, N, K, A16, K, S4, B16, K, S4, Y16, N, None, 0, None)
+
+
+def test_shape_errors():
+    assert smm(M=-1) == ST["shape"]
+    assert smm(N=-3) == ST["shape"]
+    assert smm(K=0) == ST["shape"]
+    assert smm(K=24) == ST["shape"]                     # K % 16 != 0
+    assert smm(dt=q.INT8, K=131072) == ST["shape"]      # int32 accumulator could overflow
+    assert bmm(N=200) == ST["shape"]                    # block: N % 128
+    assert bmm(K=1040) == ST["shape"]                   # block: K % 128
+
+
+def test_empty_problems_are_noops():
+    assert smm(M=0, A=None, sA=None, B=None, sB=None, Y=None) == ST["ok"]
+    assert smm(N=0, A=None, sA=None, B=None, sB=None, Y=None) == ST["ok"]
+
+
+def test_null_pointer_errors():
+    assert smm(A=None) == ST["null"]
+    assert smm(B=None) == ST["null"]
+    assert smm(sA=None) == ST["null"]
+    assert smm(sB=None) == ST["null"]
+    assert smm(Y=None) == ST["null"]
+
+
+def test_stride_and_alignment_errors():
+    assert smm(lda=512) == ST["stride"]
+    assert smm(lda=1032) == ST["stride"]                # not a multiple of 16
+    assert smm(ldb=1000) == ST["stride"]
+    assert smm(ldy=100) == ST["stride"]
+    assert smm(A=A16 + 1) == ST["align"]
+    assert smm(B=B16 + 8) == ST["align"]
+    assert smm(Y=Y16 + 2) == ST["align"]
+    assert smm(sA=S4 + 2) == ST["align"]
+
+
+def test_bad_enum():
+    assert smm(dt=7) == ST["arg"]
+
+
+def some_stream_cfg(fmt="int8"):
+    for c in q.instances_for(fmt):
+        if c.kernel == q.KERNEL_STREAM:
+            return c
+    raise AssertionError("no stream instance")
+
+
+def test_explicit_config_errors():
+    c = some_stream_cfg()
+    assert smm(cfg=c.replace(split_k=3)) == ST["cfg"]
+    assert smm(cfg=c.replace(split_k=512)) == ST["cfg"]
+    assert smm(K=256, cfg=c.replace(split_k=4)) == ST["cfg"]        # more splits than 128-byte steps
+    assert smm(cfg=c.replace(reduce=5)) == ST["cfg"]
+    assert smm(cfg=c.replace(tile_n=48)) == ST["cfg"]               # no such instance
+    # last-arriver needs one counter per output tile inside the 128 KiB region
+    many = c.replace(split_k=2, reduce=q.REDUCE_LAST_ARRIVER)
+    assert smm(M=16 * 2048, N=c.tile_n * 32, cfg=many, ws=0x50000, wsb=1 << 40) == ST["cfg"]
+    tile = [x for x in q.instances_for("int8") if x.kernel == q.KERNEL_TILE][0]
+    assert smm(M=256, K=1040, cfg=tile) == ST["cfg"]                # tile kernel needs K % 128 == 0
+    # block-scaled configs exist only as built for that format
+    blk = q.instances_for("block_fp8")
+    std_tile_fp8 = [x for x in q.instances_for("fp8") if x.kernel == q.KERNEL_TILE and x.variant == 0][0]
+    assert std_tile_fp8 not in blk
+
+
+def test_workspace_errors_and_size():
+    c = some_stream_cfg().replace(split_k=4, reduce=q.REDUCE_LAST_ARRIVER)
+    need = q.workspace_size("int8", 16, 256, 1024, c)
+    rnd = lambda v: (v + 255) // 256 * 256
+    counters = 128 * 1024                   # fixed counter region, then the partials
+    assert need == counters + rnd(4 * 16 * 256 * 4)
+    assert q.workspace_size("int8", 16, 256, 1024, c.replace(reduce=q.REDUCE_TWO_PASS)) == need
+    assert q.workspace_size("int8", 16, 256, 1024, c.replace(split_k=1)) == 0
+    assert smm(cfg=c) == ST["ws"]
+    assert smm(cfg=c, ws=0x50000, wsb=need - 1) == ST["ws"]
+    assert smm(cfg=c, ws=0x50008, wsb=need) == ST["align"]
+
+
+def test_every_instance_is_accepted_for_a_compatible_shape():
+    for cfg, mask in q.kernel_instances():
+        for fmt, bit in (("fp8", 1), ("int8", 2), ("block_fp8", 4)):
+            if mask & bit:
+                assert q.check_config(fmt, 64, 256, 1024, cfg) == 0, (fmt, cfg)
+
+
+def test_default_selection_covers_all_workload_shapes():
+    import synth
+    for name in synth.WORKLOADS:
+        for fmt, M, N, K in synth.workload(name):
+            c = q.select_config(fmt, M, N, K)
+            assert q.check_config(fmt, M, N, K, c) == 0, (fmt, M, N, K, c)
+            assert 1 <= c.split_k <= 256 and c.split_k & (c.split_k - 1) == 0
+
+
+def test_config_table_file(tmp_path):
+    c = some_stream_cfg("fp8")
+    line = lambda M, split: (f"fp8 4096 2048 {M} {c.kernel} {c.variant} {c.tile_m} {c.tile_n} "
+                             f"{c.tile_k} {c.waves_n} {c.waves_k} {c.stages} {split} 1\n")
+    p = tmp_path / "t.cfg"
+    p.write_text("# comment\n\n" + line(8, 2) + line(32, 4) + "  # trailing\n")
+    base = q.config_table_size()
+    q.load_config_table(str(p))
+    try:
+        assert q.config_table_size() == 2
+        assert q.select_config("fp8", 1, 4096, 2048).split_k == 2     # smallest tuned M >= 1
+        assert q.select_config("fp8", 8, 4096, 2048).split_k == 2
+        assert q.select_config("fp8", 9, 4096, 2048).split_k == 4
+        assert q.select_config("fp8", 500, 4096, 2048).split_k == 4   # beyond: the largest M
+        bad = tmp_path / "bad.cfg"
+        bad.write_text("fp8 4096 2048 8 0 1\n")
+        with pytest.raises(q.QlinError) as e:
+            q.load_config_table(str(bad))
+        assert e.value.status == ST["file"]
+        assert q.config_table_size() == 2                            # previous table kept
+        with pytest.raises(q.QlinError):
+            q.load_config_table(str(tmp_path / "missing.cfg"))
+        bad.write_text("fp16 4096 2048 8 0 1 16 64 256 2 2 2 1 1\n")
+        with pytest.raises(q.QlinError):
+            q.load_config_table(str(bad))
+    finally:
+        q.load_config_table(None)
+    assert q.config_table_size() == base
+
+
+def test_status_strings():
+    lib = q.lib()
+    for s in range(10):
+        assert lib.qlin_status_string(s)
