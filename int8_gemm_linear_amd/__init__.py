@@ -2,8 +2,8 @@
 
 Thin Python binding over the C ABI of ``libqlinear.so`` (``include/qlinear.h``):
 argument marshalling only.  Every step of the computation runs in the HIP
-kernels of the library; there is no CPU or PyTorch fallback, and importing
-this package fails loudly when the library has not been built
+kernels of the library; there is no CPU or PyTorch fallback, and every call
+raises ImportError when the library has not been built
 (``python -m int8_gemm_linear_amd.build``).  PyTorch supplies device memory
 and the current stream.
 
@@ -141,19 +141,26 @@ def lib():
 
 
 # ---------------------------------------------------------------------------
-# Workspace: one zeroed device buffer per (device, stream), grown on demand.
-# The split-K counters in it are left zeroed by every call.
+# Workspace: one zeroed device buffer per device, grown on demand (its split-K
+# counter region is left zeroed by every call).  Calls that may run
+# concurrently on different streams must pass their own `workspace=`.  It is
+# never grown while a HIP graph is being captured: make one eager call with
+# the same shape first, or pass a workspace.
 # ---------------------------------------------------------------------------
 _WS: dict = {}
 
 
-def workspace_for(nbytes: int, device: torch.device, stream) -> torch.Tensor | None:
+def workspace_for(nbytes: int, device: torch.device, stream=None) -> torch.Tensor | None:
     if nbytes == 0:
         return None
-    key = (device.index, int(stream.cuda_stream))
+    key = device.index if device.index is not None else torch.cuda.current_device()
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("the split-K workspace would have to grow during HIP graph capture; "
+                               "run the call once eagerly first or pass workspace=")
         buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        torch.cuda.current_stream(device).synchronize()
         _WS[key] = buf
     return buf
 

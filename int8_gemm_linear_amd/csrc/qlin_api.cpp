@@ -204,20 +204,22 @@ qlin_config default_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
         c.waves_k = 2;
         c.stages = 2;
     } else {
+        // 16 weight rows per workgroup, 4 waves splitting K, 4 steps of loads
+        // in flight per wave: the shape the sweep picks for most decode points.
         c.kernel = QLIN_KERNEL_STREAM;
         c.variant = QLIN_SWAP_AB;
         c.tile_m = M <= 16 ? 16 : 32;
-        c.tile_n = 64;
-        c.tile_k = 256;
-        c.waves_n = 2;
-        c.waves_k = 2;
+        c.tile_n = 16;
+        c.tile_k = 512;
+        c.waves_n = 1;
+        c.waves_k = 4;
         c.stages = 2;
     }
     int64_t gx, gy;
     grid_of(c, M, N, &gx, &gy);
     const int64_t kw = c.kernel == QLIN_KERNEL_STREAM ? c.waves_k : 1;
     int split = 1;
-    while (gx * gy * split < 512 && split * 2 <= 256 && split * 2 * kw <= KS)
+    while (gx * gy * split < 256 && split * 2 <= 256 && split * 2 * kw <= KS)
         split *= 2;
     c.split_k = split;
     c.reduce = gx * gy <= kMaxCounters ? QLIN_REDUCE_LAST_ARRIVER : QLIN_REDUCE_TWO_PASS;

@@ -26,10 +26,10 @@ __device__ inline v4i zero4i() { return v4i{0, 0, 0, 0}; }
 // One 128-byte K step of a 16x16 output block on the matrix cores.
 //
 // Operand layout (verified on gfx950 for both instructions): lane l feeds
-// row (l % 16) of its operand and holds 32 bytes of K, the bytes
-// [32*(l/16), 32*(l/16)+32) of the step, as x0 (first 16) and x1 (next 16).
-// The A-side and B-side operands use the same lane -> K mapping, so the
-// K sum is complete whatever slot order the hardware uses inside a lane.
+// row (l % 16) of its operand and holds 32 bytes of the step's K, as two
+// 16-byte pieces x0 and x1 (which bytes is up to the caller).  The A-side
+// and B-side operands use the same lane -> K mapping, so the K sum is
+// complete whatever slot order the hardware uses inside a lane.
 //   int8: two v_mfma_i32_16x16x64_i8 (x0 pair, then x1 pair), exact int32.
 //   e4m3: one v_mfma_f32_16x16x128_f8f6f4 (format 0 = OCP e4m3, no block
 //         scaling), fp32 accumulate.
@@ -165,6 +165,52 @@ __device__ inline void store_final4(const KArgs &p, int t, int n,
 #pragma unroll
         for (int j = 0; j < 4; ++j) d[j] = h[j];
     }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K exchange between workgroups on different XCDs.  The L2 of each XCD
+// is not coherent with the others, and an agent-scope fence (__threadfence)
+// compiles to a write-back plus invalidate of the whole L2, which costs tens
+// of microseconds when every workgroup issues it.  Instead the partials are
+// written and read with agent-scope atomic stores/loads (device-coherent
+// accesses that do not leave stale or dirty lines in a non-coherent L2), and
+// the writer waits for its own stores to be acknowledged before the counter
+// increment.  The last arriver observes the final counter value through an
+// agent-scope atomic, then reads every partial with agent-scope loads.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ inline void st_dev(T *p, T v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T>
+__device__ inline T ld_dev(T *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every thread of the workgroup calls this after writing its partials with
+// st_dev.  Returns true (in all threads) for the workgroup whose increment
+// brought the tile's counter to split_k.
+__device__ inline bool arrive_last(int32_t *counter, int split_k)
+{
+    __shared__ int s_last;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // own partial stores acknowledged
+    __syncthreads();
+    if (threadIdx.x == 0)
+        s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 split_k - 1;
+    __syncthreads();
+    return s_last != 0;
+}
+
+// The last arriver re-arms the counter for the next call (stream order makes
+// it visible to the next launch).
+__device__ inline void rearm(int32_t *counter)
+{
+    if (threadIdx.x == 0)
+        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Partials: [split][M][N], 4-byte elements, row stride N.

@@ -5,10 +5,12 @@
 // tokens of one K split.  Its WN x WK waves split the rows (WN) and the
 // split's K range (WK).  Every weight byte is used by exactly one matrix-core
 // instruction, so B goes straight from HBM into registers with 16-byte
-// non-temporal loads in the matrix-core operand layout (each lane reads 32
-// contiguous bytes of one row per 128-byte K step; a 16-row block reads 16 x
-// 128 contiguous bytes), double-buffered U steps deep so 2*U*RB steps of
-// loads stay in flight per wave.  Staging B through LDS would add traffic and
+// non-temporal loads in the matrix-core operand layout, double-buffered U
+// steps deep so 2*U*RB steps of loads stay in flight per wave.  Within a
+// 128-byte K step, lane group g = lane/16 feeds the matrix core the bytes
+// [16g, 16g+16) as its first 16-byte piece and [64+16g, 64+16g+16) as its
+// second, so each load instruction reads 64 contiguous bytes of each of its
+// 16 rows (A uses the same assignment, so every K slot pairs the same k).  Staging B through LDS would add traffic and
 // a barrier per step without any reuse to pay for it.  The small activation
 // tile A (tokens) is re-read from L1/L2 by each wave.
 //
@@ -78,7 +80,7 @@ k_stream(KArgs p)
     for (int rb = 0; rb < RB; ++rb) {
         const int n = nw0 + rb * 16 + r16;
         bok[rb] = n < p.N;
-        brow[rb] = p.B + (int64_t)(bok[rb] ? n : 0) * p.ldb + g * 32;
+        brow[rb] = p.B + (int64_t)(bok[rb] ? n : 0) * p.ldb + g * 16;
         nb[rb] = (nw0 + rb * 16) >> 7;
     }
     const uint8_t *arow[TB];
@@ -87,7 +89,7 @@ k_stream(KArgs p)
     for (int tb = 0; tb < TB; ++tb) {
         const int t = m0 + tb * 16 + r16;
         aok[tb] = t < p.M;
-        arow[tb] = p.A + (int64_t)(aok[tb] ? t : 0) * p.lda + g * 32;
+        arow[tb] = p.A + (int64_t)(aok[tb] ? t : 0) * p.lda + g * 16;
     }
 
     A4 acc[RB][TB];
@@ -107,15 +109,15 @@ k_stream(KArgs p)
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const bool ok = sv && bok[rb] && (kb + g * 32 + h * 16 < p.K);
-                    f.b[u][rb][h] = ok ? ld_nt(brow[rb] + kb + h * 16) : zero4i();
+                    const bool ok = sv && bok[rb] && (kb + h * 64 + g * 16 < p.K);
+                    f.b[u][rb][h] = ok ? ld_nt(brow[rb] + kb + h * 64) : zero4i();
                 }
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const bool ok = sv && aok[tb] && (kb + g * 32 + h * 16 < p.K);
-                    f.a[u][tb][h] = ok ? ld16(arow[tb] + kb + h * 16) : zero4i();
+                    const bool ok = sv && aok[tb] && (kb + h * 64 + g * 16 < p.K);
+                    f.a[u][tb][h] = ok ? ld16(arow[tb] + kb + h * 64) : zero4i();
                 }
             if constexpr (SCAL == SC_BLOCK) {
 #pragma unroll
@@ -256,54 +258,37 @@ k_stream(KArgs p)
         return;
     }
 
-    // Split-K: write this split's partial sums.
+    // Split-K: write this split's partial sums.  For the two-pass reduction
+    // plain stores suffice (the kernel boundary orders them before the
+    // second pass); the last-arriver exchange uses device-coherent stores.
+    const bool la = p.reduce == QLIN_REDUCE_LAST_ARRIVER;
     if (wk == 0) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
-                if (SWAP) {
-                    const int t = m0 + tb * 16 + r16;
-                    const int n = nw0 + rb * 16 + 4 * g;
-                    if (t >= p.M)
-                        continue;
-                    AS *d = part_ptr<FMT>(p, split, t, n);
-                    if (n + 3 < p.N && (p.N & 3) == 0) {
-                        *reinterpret_cast<A4 *>(d) = acc[rb][tb];
-                    } else {
 #pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            if (n + v < p.N)
-                                d[v] = acc[rb][tb][v];
-                    }
-                } else {
-                    const int n = nw0 + rb * 16 + r16;
-                    if (n >= p.N)
-                        continue;
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int t = m0 + tb * 16 + 4 * g + v;
-                        if (t < p.M)
-                            *part_ptr<FMT>(p, split, t, n) = acc[rb][tb][v];
+                for (int v = 0; v < 4; ++v) {
+                    const int t = SWAP ? m0 + tb * 16 + r16 : m0 + tb * 16 + 4 * g + v;
+                    const int n = SWAP ? nw0 + rb * 16 + 4 * g + v : nw0 + rb * 16 + r16;
+                    if (t < p.M && n < p.N) {
+                        AS *d = part_ptr<FMT>(p, split, t, n);
+                        if (la)
+                            st_dev(d, (AS)acc[rb][tb][v]);
+                        else
+                            *d = acc[rb][tb][v];
                     }
                 }
             }
     }
-    if (p.reduce != QLIN_REDUCE_LAST_ARRIVER)
+    if (!la)
         return;
 
     // Last arriver: the final split to finish sums all partials of the tile
     // in split order 0..split_k-1 and applies the epilogue.
-    __shared__ int s_last;
-    __threadfence();
-    __syncthreads();
     const int tile = blockIdx.y * gridDim.x + blockIdx.x;
-    if (threadIdx.x == 0)
-        s_last = atomicAdd(&p.counters[tile], 1) == p.split_k - 1;
-    __syncthreads();
-    if (!s_last)
+    if (!arrive_last(p.counters + tile, p.split_k))
         return;
-    __threadfence();
     if (wk == 0) {
         A4 sum[RB][TB];
 #pragma unroll
@@ -317,14 +302,13 @@ k_stream(KArgs p)
                         const int t = SWAP ? m0 + tb * 16 + r16 : m0 + tb * 16 + 4 * g + v;
                         const int n = SWAP ? nw0 + rb * 16 + 4 * g + v : nw0 + rb * 16 + r16;
                         if (t < p.M && n < p.N)
-                            sum[rb][tb][v] += *part_ptr<FMT>(p, s, t, n);
+                            sum[rb][tb][v] += ld_dev(part_ptr<FMT>(p, s, t, n));
                     }
                 }
             }
         emit(sum);
     }
-    if (threadIdx.x == 0)
-        atomicExch(&p.counters[tile], 0);
+    rearm(p.counters + tile);
 }
 
 template <int FMT, int SCAL, bool SWAP, int TB, int RB, int WN, int WK, int U>
@@ -342,6 +326,10 @@ hipError_t launch_stream(const KArgs &a, dim3 grid, hipStream_t s)
 // The shape list shared by the three formats: (RB, WN, WK, U).
 #define QLIN_STREAM_SHAPES(X, FMT, SCAL, BIT, SW, TB) \
     X(FMT, SCAL, BIT, SW, TB, 1, 1, 4, 4),            \
+    X(FMT, SCAL, BIT, SW, TB, 1, 1, 4, 8),            \
+    X(FMT, SCAL, BIT, SW, TB, 1, 1, 8, 2),            \
+    X(FMT, SCAL, BIT, SW, TB, 1, 1, 8, 4),            \
+    X(FMT, SCAL, BIT, SW, TB, 2, 1, 8, 2),            \
     X(FMT, SCAL, BIT, SW, TB, 1, 2, 2, 4),            \
     X(FMT, SCAL, BIT, SW, TB, 1, 4, 1, 4),            \
     X(FMT, SCAL, BIT, SW, TB, 2, 1, 4, 2),            \
@@ -350,7 +338,13 @@ hipError_t launch_stream(const KArgs &a, dim3 grid, hipStream_t s)
     X(FMT, SCAL, BIT, SW, TB, 4, 1, 4, 1),            \
     X(FMT, SCAL, BIT, SW, TB, 4, 2, 2, 1)
 
+// 16 waves (1024 threads) leave 128 registers per lane: one token block only.
+#define QLIN_STREAM_SHAPES_TB1(X, FMT, SCAL, BIT, SW) \
+    X(FMT, SCAL, BIT, SW, 1, 1, 1, 16, 2)
+
 #define QLIN_STREAM_ALL(FMT, SCAL, BIT)                                   \
+    QLIN_STREAM_SHAPES_TB1(QLIN_STREAM_INSTANCE, FMT, SCAL, BIT, 0),      \
+    QLIN_STREAM_SHAPES_TB1(QLIN_STREAM_INSTANCE, FMT, SCAL, BIT, 1),      \
     QLIN_STREAM_SHAPES(QLIN_STREAM_INSTANCE, FMT, SCAL, BIT, 0, 1),       \
     QLIN_STREAM_SHAPES(QLIN_STREAM_INSTANCE, FMT, SCAL, BIT, 0, 2),       \
     QLIN_STREAM_SHAPES(QLIN_STREAM_INSTANCE, FMT, SCAL, BIT, 1, 1),       \

@@ -258,7 +258,8 @@ k_tile(KArgs p)
         return;
     }
 
-    // Split-K partials
+    // Split-K partials (device-coherent stores for the last-arriver exchange)
+    const bool la = p.reduce == QLIN_REDUCE_LAST_ARRIVER;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -269,23 +270,21 @@ k_tile(KArgs p)
             for (int v = 0; v < 16; ++v) {
                 const int t = SWAP ? tok0 + fr : tok0 + 8 * (v >> 2) + 4 * fh + (v & 3);
                 const int n = SWAP ? wgt0 + 8 * (v >> 2) + 4 * fh + (v & 3) : wgt0 + fr;
-                if (t < p.M && n < p.N)
-                    *part_ptr<FMT>(p, split, t, n) = acc[fm][fn][v];
+                if (t < p.M && n < p.N) {
+                    AS *d = part_ptr<FMT>(p, split, t, n);
+                    if (la)
+                        st_dev(d, (AS)acc[fm][fn][v]);
+                    else
+                        *d = acc[fm][fn][v];
+                }
             }
         }
-    if (p.reduce != QLIN_REDUCE_LAST_ARRIVER)
+    if (!la)
         return;
 
-    __shared__ int s_last;
-    __threadfence();
-    __syncthreads();
     const int tile = blockIdx.x;
-    if (threadIdx.x == 0)
-        s_last = atomicAdd(&p.counters[tile], 1) == p.split_k - 1;
-    __syncthreads();
-    if (!s_last)
+    if (!arrive_last(p.counters + tile, p.split_k))
         return;
-    __threadfence();
     A16 sum[FM][FN];
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
@@ -300,13 +299,12 @@ k_tile(KArgs p)
                 AS a = 0;
                 if (t < p.M && n < p.N)
                     for (int s = 0; s < p.split_k; ++s)
-                        a += *part_ptr<FMT>(p, s, t, n);
+                        a += ld_dev(part_ptr<FMT>(p, s, t, n));
                 sum[fm][fn][v] = a;
             }
         }
     emit(sum);
-    if (threadIdx.x == 0)
-        atomicExch(&p.counters[tile], 0);
+    rearm(p.counters + tile);
 }
 
 template <int FMT, int SCAL, bool SWAP, int BM, int BN, int WM, int WN>

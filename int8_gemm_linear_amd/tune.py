@@ -1,0 +1,220 @@
+"""Offline per-shape tuning sweep on the MI355X.
+
+The pages replace hand-written dispatch rules (for instance "use Swap-AB
+below 32 tokens") by a per-shape ahead-of-time search over the algorithm
+variant and the low-level launch configuration ("Building a High-Performance
+and Portable vLLM Linear Backend with Helion", section "Kernel
+Implementation"; the techfeed.io summary gives the tunable domains, split_k a
+power of two in [1, 256] and swap_ab a boolean).  Our search space is small
+enough to sweep exhaustively: every built kernel instance x variant x split_k
+x reduction mode that is valid for the shape.
+
+Each candidate is timed as the pages time theirs, under graph replay: a HIP
+graph of R launches, each on a different copy of the weights (together
+larger than the 256 MB Infinity Cache, so weights come from HBM), replayed a
+few times; the per-launch time is the median replay time / R.  A candidate
+whose output differs from the reference candidate's is discarded (INT8: bit
+for bit; FP8: relative difference above 2^-6).
+
+    python -m int8_gemm_linear_amd.tune --workload int8_1p7b_decode \
+        --jsonl tune.jsonl --table int8_gemm_linear_amd/configs/qlin_mi355x.cfg
+
+Results are appended to the JSONL log and a restart skips finished
+(point, candidate) pairs.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import int8_gemm_linear_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+COLD_BYTES = 512 << 20
+
+
+def candidates(fmt: str, M: int, N: int, K: int, max_split: int = 256):
+    """Every valid (instance, split_k, reduce) for the point."""
+    out = []
+    KS = -(-K // 128)
+    for base in q.instances_for(fmt):
+        if base.kernel == q.KERNEL_STREAM and -(-M // base.tile_m) > 4:
+            continue                      # the stream kernel is for small token counts
+        if base.kernel == q.KERNEL_TILE and M < 32:
+            continue
+        split = 1
+        while split <= min(max_split, 256):
+            kw = base.waves_k if base.kernel == q.KERNEL_STREAM else 1
+            if split * kw > KS:
+                break
+            reds = (q.REDUCE_LAST_ARRIVER,) if split == 1 else (q.REDUCE_LAST_ARRIVER, q.REDUCE_TWO_PASS)
+            for r in reds:
+                c = base.replace(split_k=split, reduce=r)
+                if q.check_config(fmt, M, N, K, c) == 0:
+                    out.append(c)
+            split *= 2
+    return out
+
+
+class Point:
+    """Device inputs of one (fmt, M, N, K) with enough weight copies to be cold."""
+
+    def __init__(self, fmt, M, N, K, cold_bytes=COLD_BYTES, root=0):
+        sys.path.insert(0, ROOT)
+        import synth
+        self.fmt, self.M, self.N, self.K = fmt, M, N, K
+        case = synth.make_case(fmt, M, N, K, root=root)
+        dt = torch.int8 if fmt == "int8" else torch.float8_e4m3fn
+        dev = torch.device("cuda")
+        self.a = torch.from_numpy(np.ascontiguousarray(case.A)).to(dev).view(dt)
+        self.sa = torch.from_numpy(np.ascontiguousarray(case.sA)).to(dev)
+        b = torch.from_numpy(np.ascontiguousarray(case.B)).to(dev).view(dt)
+        self.sb = torch.from_numpy(np.ascontiguousarray(case.sB)).to(dev)
+        ncopy = int(min(256, max(2, -(-cold_bytes // (N * K)))))
+        self.b = [b] + [b.clone() for _ in range(ncopy - 1)]
+        self.y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = max(q.workspace_size(fmt, M, N, K, c) for c in candidates(fmt, M, N, K)) \
+            if M > 0 else 0
+        self.ws = torch.zeros(max(ws, 1 << 20), dtype=torch.uint8, device=dev)
+
+    def call(self, cfg, i=0, out=None):
+        f = q.block_scaled_mm if self.fmt == "block_fp8" else q.scaled_mm
+        return f(self.a, self.sa, self.b[i % len(self.b)], self.sb, out=self.y if out is None else out,
+                 config=cfg, workspace=self.ws)
+
+    def time(self, cfg, reps: int | None = None, replays: int = 3) -> float:
+        """Median per-launch microseconds over `replays` replays of an R-launch graph."""
+        R = reps or len(self.b)
+        self.call(cfg)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(R):
+                self.call(cfg, i)
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(replays):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3 / R)
+        del g
+        return float(np.median(ts))
+
+
+def agree(fmt, y, ref) -> bool:
+    if fmt == "int8":
+        return torch.equal(y.view(torch.int16), ref.view(torch.int16))
+    d = (y.float() - ref.float()).abs()
+    return bool((d <= ref.float().abs() * 2.0 ** -6 + 1e-30).all() or d.max().item() == 0)
+
+
+def tune_point(fmt, M, N, K, log=None, done=None, max_cands=None, verbose=False):
+    pt = Point(fmt, M, N, K)
+    cands = candidates(fmt, M, N, K)
+    if max_cands:
+        cands = cands[:max_cands]
+    ref = pt.call(q.select_config(fmt, M, N, K), out=torch.empty_like(pt.y)).clone()
+    torch.cuda.synchronize()
+    results = []
+    for c in cands:
+        key = json.dumps([fmt, M, N, K, list(c.__dict__.values())])
+        if done is not None and key in done:
+            results.append((done[key]["us"], c, done[key]["ok"]))
+            continue
+        y = pt.call(c, out=torch.full_like(pt.y, float("nan")))
+        torch.cuda.synchronize()
+        ok = agree(fmt, y, ref)
+        us = pt.time(c) if ok else float("inf")
+        results.append((us, c, ok))
+        if log is not None:
+            log.write(json.dumps({"key": key, "fmt": fmt, "M": M, "N": N, "K": K,
+                                  "cfg": c.__dict__, "us": us, "ok": ok}) + "\n")
+            log.flush()
+        if verbose:
+            print(f"  {us:9.2f} us ok={ok} {c}", flush=True)
+    results.sort(key=lambda r: r[0])
+    del pt
+    torch.cuda.empty_cache()
+    return results
+
+
+def table_line(fmt, M, N, K, c) -> str:
+    return (f"{fmt} {N} {K} {M} {c.kernel} {c.variant} {c.tile_m} {c.tile_n} {c.tile_k} "
+            f"{c.waves_n} {c.waves_k} {c.stages} {c.split_k} {c.reduce}")
+
+
+def alg_bytes(fmt, M, N, K):
+    s = 4 * M * (K // 128) + 4 * (N // 128) * (K // 128) if fmt == "block_fp8" else 4 * (M + N)
+    return M * K + N * K + 2 * M * N + s
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", action="append", default=[])
+    ap.add_argument("--point", action="append", default=[], help="fmt,M,N,K")
+    ap.add_argument("--jsonl", default=None)
+    ap.add_argument("--table", default=None, help="write/merge the best configs into this table")
+    ap.add_argument("--max-cands", type=int, default=None)
+    ap.add_argument("--verbose", action="store_true")
+    args = ap.parse_args()
+    sys.path.insert(0, ROOT)
+    import synth
+
+    points = []
+    for w in args.workload:
+        points += synth.workload(w)
+    for p in args.point:
+        f, M, N, K = p.split(",")
+        points.append((f, int(M), int(N), int(K)))
+    done = {}
+    if args.jsonl and os.path.exists(args.jsonl):
+        for ln in open(args.jsonl):
+            try:
+                r = json.loads(ln)
+                done[r["key"]] = r
+            except ValueError:
+                pass
+    log = open(args.jsonl, "a") if args.jsonl else None
+    best = {}
+    t0 = time.time()
+    for (fmt, M, N, K) in points:
+        res = tune_point(fmt, M, N, K, log=log, done=done, max_cands=args.max_cands,
+                         verbose=args.verbose)
+        us, c, _ = res[0]
+        dflt = q.select_config(fmt, M, N, K)
+        dus = next((r[0] for r in res if r[1] == dflt), float("nan"))
+        best[(fmt, M, N, K)] = c
+        print(f"[tune] {fmt:9s} M={M:5d} N={N:6d} K={K:6d}: best {us:8.2f} us "
+              f"({alg_bytes(fmt, M, N, K) / us / 1e6:.3f} TB/s, {2 * M * N * K / us / 1e6:.1f} TFLOP/s) "
+              f"default {dus:8.2f} us | {len(res)} cands | {table_line(fmt, M, N, K, c)} "
+              f"[{time.time() - t0:.0f}s]", flush=True)
+    if args.table:
+        lines = {}
+        if os.path.exists(args.table):
+            for ln in open(args.table):
+                s = ln.split("#")[0].split()
+                if len(s) == 14:
+                    lines[(s[0], int(s[3]), int(s[1]), int(s[2]))] = ln.strip()
+        for (fmt, M, N, K), c in best.items():
+            lines[(fmt, M, N, K)] = table_line(fmt, M, N, K, c)
+        hdr = [ln.rstrip("\n") for ln in open(args.table) if ln.startswith("#")] \
+            if os.path.exists(args.table) else []
+        with open(args.table, "w") as f:
+            f.write("\n".join(hdr) + "\n")
+            for k in sorted(lines):
+                f.write(lines[k] + "\n")
+
+
+if __name__ == "__main__":
+    main()
