@@ -98,7 +98,10 @@ typedef enum qlin_scaling {
 
 typedef enum qlin_kernel {
     QLIN_KERNEL_STREAM = 0,     /* weights streamed HBM -> registers; small M */
-    QLIN_KERNEL_TILE = 1        /* A and B tiles staged through a double-buffered LDS ring; large M */
+    QLIN_KERNEL_TILE = 1,       /* A and B tiles staged through a double-buffered LDS ring; large M */
+    QLIN_KERNEL_STREAM_LDS = 2  /* weights and tokens copied HBM -> LDS in 1 KB row segments
+                                   through a multi-stage ring; small M; K % 256 == 0;
+                                   token/channel scaling only */
 } qlin_kernel;
 
 typedef enum qlin_variant {
@@ -114,7 +117,10 @@ typedef enum qlin_reduce {
 /* One launch configuration.  For the STREAM kernel: tile_m = tokens per
  * workgroup (16 or 32), tile_n = weight rows per workgroup, tile_k = K bytes
  * each wave loads per pipeline step (multiple of 128), waves_n x waves_k
- * waves split the tile's rows and the split's K range.  For the TILE kernel:
+ * waves split the tile's rows and the split's K range.  For STREAM_LDS:
+ * tile_m / tile_n as for STREAM, tile_k = bytes per row per LDS chunk (512
+ * or 1024), waves_k waves share each chunk's K steps, stages = ring depth.
+ * For the TILE kernel:
  * tile_m x tile_n output tile, tile_k = 128, waves_n x waves_k is the wave
  * grid over the tile (rows x columns).  split_k is 1..256, a power of two;
  * each split covers a contiguous, 128-aligned K range.  stages is the

@@ -27,6 +27,8 @@ SOURCES = [
     "qlin_tile_fp8.hip",
     "qlin_tile_int8.hip",
     "qlin_tile_block.hip",
+    "qlin_stream_lds_fp8.hip",
+    "qlin_stream_lds_int8.hip",
 ]
 
 ARCH = "gfx950"

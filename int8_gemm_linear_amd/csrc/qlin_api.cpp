@@ -53,6 +53,7 @@ const std::vector<Instance> &registry()
         const Instance *(*fns[])(int *) = {
             stream_instances_fp8, stream_instances_int8, stream_instances_block,
             tile_instances_fp8, tile_instances_int8, tile_instances_block,
+            stream_lds_instances_fp8, stream_lds_instances_int8,
         };
         for (auto f : fns) {
             int n = 0;
@@ -259,6 +260,8 @@ qlin_status check_config(int fmt, int scal, int64_t M, int64_t N, int64_t K,
         return QLIN_ERR_BAD_CONFIG;
     if (c.kernel == QLIN_KERNEL_TILE && K % 128 != 0)
         return QLIN_ERR_BAD_CONFIG;   // the LDS ring copies whole 128-byte K steps
+    if (c.kernel == QLIN_KERNEL_STREAM_LDS && (K % 256 != 0 || c.split_k > K / 256))
+        return QLIN_ERR_BAD_CONFIG;   // 256-byte K units keep the LDS swizzle in range
     int64_t gx, gy;
     grid_of(c, M, N, &gx, &gy);
     if (gx > 0x7fffffff || gy > 65535)

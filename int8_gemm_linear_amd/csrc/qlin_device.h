@@ -130,6 +130,27 @@ __device__ inline void store_final(const KArgs &p, int t, int n, typename AccT<F
     p.Y[(int64_t)t * p.ldy + n] = bf16_bits(finish_value<FMT, SCAL>(p, t, n, v));
 }
 
+// Four final token/channel outputs for columns n..n+3 of row t (all in
+// range) with the scales already in registers: sa = sA[t], sb = sB[n..n+3].
+template <int FMT, int SCAL>
+__device__ inline void store_final4_pre(const KArgs &p, int t, int n,
+                                        typename AccT<FMT>::v4 v, float sa, v4f sb)
+{
+    uint16_t h[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) h[j] = bf16_bits(((float)v[j] * sa) * sb[j]);
+    uint16_t *d = p.Y + (int64_t)t * p.ldy + n;
+    if ((p.ldy & 3) == 0) {
+        uint2 w;
+        w.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+        w.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+        *reinterpret_cast<uint2 *>(d) = w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[j] = h[j];
+    }
+}
+
 // Store four final values for columns n..n+3 of row t (all in range).
 template <int FMT, int SCAL>
 __device__ inline void store_final4(const KArgs &p, int t, int n,

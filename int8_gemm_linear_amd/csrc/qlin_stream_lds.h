@@ -1,0 +1,376 @@
+// The STREAM_LDS kernel family: small token counts (decode), weight tiles
+// copied HBM -> LDS in 1 KB row segments.
+//
+// Why: on MI355X a weight stream read as 1 KB contiguous row segments per
+// load instruction runs markedly faster than the matrix-core operand layout
+// read straight into registers (16 rows x 64 bytes per instruction), and
+// global_load_lds keeps many segments in flight without holding registers.
+// The LDS round trip costs nothing that matters here: LDS bandwidth is far
+// above a CU's share of HBM bandwidth.
+//
+// Workgroup: NW waves own TR = 16*RB weight rows and TMS tokens (1..32; the
+// matrix core sees them as TB = ceil(TMS/16) blocks of 16, the rows past TMS
+// hold stale data that only feeds outputs never stored) of one K split.  The
+// split's K range is cut into chunks of CHK bytes; a chunk stage in LDS holds
+// [TR weight rows][CHK], [TMS token rows][CHK] and padding rows.  Each load
+// instruction copies 1 KB (CHK = 1024: one row segment; CHK = 512: two rows,
+// 512 bytes each) with global_load_lds_dwordx4, so every byte moves HBM/L2 ->
+// LDS in contiguous runs; padding instructions read one cache line so every
+// wave issues the same count L per chunk.  All S stages are filled up front
+// (for decode K this is usually the whole split: one round trip), and stage
+// c % S is refilled with chunk c + S after chunk c is consumed.  All global
+// loads inside the loop are these copies, so the wait for chunk c is an
+// exact s_waitcnt vmcnt(L * chunks issued after c).
+//
+// LDS swizzle: within a row, 16-byte slot s holds the chunk's 16-byte piece
+// s ^ (row & 15).  A matrix-core fragment read (16 lanes, 16 consecutive
+// rows, the same piece) then touches 16 distinct slot residues, i.e. 16
+// distinct bank groups.  The swizzle is applied on the global side (lane i
+// fetches piece i ^ (row & 15)), which keeps every instruction inside its
+// 1 KB segment, and stays inside a partial chunk because chunk lengths are
+// multiples of 256 bytes (K % 256 == 0 for this family).
+//
+// The waves split each chunk's 128-byte K steps; their partial sums are
+// combined in LDS in fixed wave order, then the epilogue (scales, bf16,
+// Swap-AB orientation, Split-K partials / last arriver) is the stream
+// kernel's.  Variants and split-K as in the "Kernel Implementation" section
+// of "Building a High-Performance and Portable vLLM Linear Backend with
+// Helion"; token/channel scaling only (Block_FP8 uses the other kernels).
+#pragma once
+
+#include "qlin_device.h"
+
+namespace qlin {
+
+template <int N>
+__device__ inline void wait_vm()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    if constexpr (N == 0)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int FMT, bool SWAP, int TMS, int RB, int NW, int S, int CHK>
+__global__ void __launch_bounds__(64 * NW)
+k_stream_lds(KArgs p)
+{
+    typedef typename AccT<FMT>::v4 A4;
+    typedef typename AccT<FMT>::scalar AS;
+    constexpr int TB = (TMS + 15) / 16;
+    constexpr int TR = 16 * RB;
+    constexpr int RPI = 1024 / CHK;                  // rows per load instruction
+    constexpr int ROWS0 = TR + TMS;
+    constexpr int INSTR = ((ROWS0 + RPI * NW - 1) / (RPI * NW)) * NW;   // padded
+    constexpr int ROWS = INSTR * RPI;
+    constexpr int STAGE = ROWS * CHK;
+    constexpr int L = INSTR / NW;                    // per wave per chunk
+    static_assert(CHK == 512 || CHK == 1024, "chunk");
+    static_assert(TMS >= 1 && TMS <= 32, "tokens per tile");
+    static_assert(S >= 1 && S <= 4 && L * (S - 1) <= 63, "ring");
+
+    __shared__ __attribute__((aligned(16))) uint8_t lds[S * STAGE];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r16 = lane & 15;
+    const int g = lane >> 4;
+
+    const int n0 = blockIdx.x * TR;
+    const int m0 = blockIdx.y * TMS;
+    const int split = blockIdx.z;
+
+    // K range of this split, in 256-byte units.
+    const int KP = p.K >> 8;
+    const int pps = (KP + p.split_k - 1) / p.split_k;
+    const int kbeg = min(KP, split * pps) * 256;
+    const int kend = min(KP, split * pps + pps) * 256;
+    const int nch = (kend - kbeg + CHK - 1) / CHK;
+
+    // Per-instruction source rows.  Padding rows, and rows past N or M (they
+    // feed only outputs that are never stored), still issue their instruction
+    // -- keeping the per-wave load count exact for the vmcnt waits -- but all
+    // lanes read the same 16 bytes: one cache line instead of a 1 KB segment.
+    const uint8_t *src[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const int ins = wave + i * NW;
+        const int j = ins * RPI + (RPI == 2 ? (lane >> 5) : 0);       // stage row
+        const int slot = RPI == 2 ? (lane & 31) : lane;
+        const bool isb = j < TR;
+        const int row = isb ? n0 + j : m0 + j - TR;
+        const bool valid = isb ? row < p.N : (j < TR + TMS && row < p.M);
+        const uint8_t *base = isb ? p.B + (int64_t)(valid ? row : 0) * p.ldb
+                                  : p.A + (int64_t)(valid ? row : 0) * p.lda;
+        src[i] = valid ? base + 16 * (slot ^ (j & 15)) : base;
+    }
+
+    auto issue = [&](int c) {
+        const int k0 = kbeg + c * CHK;
+        const int len = min(CHK, kend - k0);
+        uint8_t *st = lds + (c % S) * STAGE;
+        const int slot = RPI == 2 ? (lane & 31) : lane;
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            const int ins = wave + i * NW;
+            if (slot * 16 < len)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(src[i] + k0),
+                    (__attribute__((address_space(3))) void *)(st + ins * 1024), 16, 0, 0);
+        }
+    };
+
+    A4 acc[RB][TB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+            acc[rb][tb] = A4{0, 0, 0, 0};
+
+    // Epilogue scales of this lane's outputs, loaded before the first copy:
+    // they complete ahead of every chunk (loads return in issue order), so
+    // the chunk waits stay exact and their latency hides under the stream.
+    //   SWAP: sa1[tb] = sA[t], sb4[rb] = sB[n..n+3]
+    //   standard: sa4[tb] = sA[t..t+3], sb1[rb] = sB[n]
+    float sa1[TB], sb1[RB];
+    v4f sa4[TB], sb4[RB];
+    const bool scaled = p.acc_out == nullptr;
+    if (scaled) {
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            if (SWAP) {
+                const int t = m0 + tb * 16 + r16;
+                sa1[tb] = t < p.M ? p.sA[t] : 0.f;
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int t = m0 + tb * 16 + 4 * g + v;
+                    sa4[tb][v] = t < p.M ? p.sA[t] : 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            if (SWAP) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int n = n0 + rb * 16 + 4 * g + v;
+                    sb4[rb][v] = n < p.N ? p.sB[n] : 0.f;
+                }
+            } else {
+                const int n = n0 + rb * 16 + r16;
+                sb1[rb] = n < p.N ? p.sB[n] : 0.f;
+            }
+        }
+    }
+
+    for (int c = 0; c < S && c < nch; ++c)
+        issue(c);
+
+    // Token row of the stage a fragment lane reads (rows past TMS alias the
+    // first token row: their outputs are never stored).
+    int arow[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+        arow[tb] = TR + (tb * 16 + r16 < TMS ? tb * 16 + r16 : 0);
+
+    for (int c = 0; c < nch; ++c) {
+        const int after = min(S - 1, nch - 1 - c);   // chunks issued after c
+        if (after >= 3)
+            wait_vm<L * 3>();
+        else if (after == 2)
+            wait_vm<L * 2>();
+        else if (after == 1)
+            wait_vm<L>();
+        else
+            wait_vm<0>();
+        __syncthreads();
+        const uint8_t *st = lds + (c % S) * STAGE;
+        const int steps = min(CHK, kend - (kbeg + c * CHK)) >> 7;
+        for (int s = wave; s < steps; s += NW) {
+            v4i bf[RB][2], af[TB][2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int piece = s * 8 + h * 4 + g;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    bf[rb][h] = *reinterpret_cast<const v4i *>(st + (rb * 16 + r16) * CHK +
+                                                                16 * (piece ^ r16));
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb)
+                    af[tb][h] = *reinterpret_cast<const v4i *>(st + arow[tb] * CHK +
+                                                                16 * (piece ^ (arow[tb] & 15)));
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb)
+                    acc[rb][tb] = SWAP ? mma16<FMT>(bf[rb][0], bf[rb][1], af[tb][0], af[tb][1], acc[rb][tb])
+                                       : mma16<FMT>(af[tb][0], af[tb][1], bf[rb][0], bf[rb][1], acc[rb][tb]);
+        }
+        if (c + S < nch) {
+            __syncthreads();                     // every wave is done with stage c % S
+            issue(c + S);
+        }
+    }
+
+    // Combine the waves' partial sums in fixed order (wave 0 first); the ring
+    // is free once every wave has passed this barrier.
+    __syncthreads();
+    if (NW > 1) {
+        AS *red = reinterpret_cast<AS *>(lds);      // [NW-1][RB*TB*4][64]
+        static_assert((NW - 1) * RB * TB * 4 * 64 * 4 <= S * STAGE, "reduction space");
+        if (wave > 0) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        red[((wave - 1) * RB * TB * 4 + (rb * TB + tb) * 4 + v) * 64 + lane] = acc[rb][tb][v];
+        }
+        __syncthreads();
+        if (wave == 0) {
+            for (int w = 1; w < NW; ++w)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            acc[rb][tb][v] += red[((w - 1) * RB * TB * 4 + (rb * TB + tb) * 4 + v) * 64 + lane];
+        }
+    }
+
+    //   SWAP:     n = n0 + 16*rb + 4*g + v,  t = m0 + 16*tb + r16
+    //   standard: n = n0 + 16*rb + r16,      t = m0 + 16*tb + 4*g + v
+    const int mend = min(p.M, m0 + TMS);           // tokens of this tile
+    auto emit = [&](const A4 (&val)[RB][TB]) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                if (SWAP) {
+                    const int t = m0 + tb * 16 + r16;
+                    const int n = n0 + rb * 16 + 4 * g;
+                    if (t >= mend)
+                        continue;
+                    if (!scaled) {
+                        if (n + 3 < p.N) {
+                            store_final4<FMT, SC_TC>(p, t, n, val[rb][tb]);
+                        } else {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v)
+                                if (n + v < p.N)
+                                    store_final<FMT, SC_TC>(p, t, n + v, val[rb][tb][v]);
+                        }
+                    } else if (n + 3 < p.N) {
+                        store_final4_pre<FMT, SC_TC>(p, t, n, val[rb][tb], sa1[tb], sb4[rb]);
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            if (n + v < p.N)
+                                p.Y[(int64_t)t * p.ldy + n + v] =
+                                    bf16_bits(((float)val[rb][tb][v] * sa1[tb]) * sb4[rb][v]);
+                    }
+                } else {
+                    const int n = n0 + rb * 16 + r16;
+                    if (n >= p.N)
+                        continue;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int t = m0 + tb * 16 + 4 * g + v;
+                        if (t >= mend)
+                            continue;
+                        if (!scaled)
+                            store_final<FMT, SC_TC>(p, t, n, val[rb][tb][v]);
+                        else
+                            p.Y[(int64_t)t * p.ldy + n] =
+                                bf16_bits(((float)val[rb][tb][v] * sa4[tb][v]) * sb1[rb]);
+                    }
+                }
+            }
+    };
+
+    if (p.split_k == 1) {
+        if (wave == 0)
+            emit(acc);
+        return;
+    }
+
+    const bool la = p.reduce == QLIN_REDUCE_LAST_ARRIVER;
+    if (wave == 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int t = SWAP ? m0 + tb * 16 + r16 : m0 + tb * 16 + 4 * g + v;
+                    const int n = SWAP ? n0 + rb * 16 + 4 * g + v : n0 + rb * 16 + r16;
+                    if (t < mend && n < p.N) {
+                        AS *d = part_ptr<FMT>(p, split, t, n);
+                        if (la)
+                            st_dev(d, (AS)acc[rb][tb][v]);
+                        else
+                            *d = acc[rb][tb][v];
+                    }
+                }
+    }
+    if (!la)
+        return;
+    const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+    if (!arrive_last(p.counters + tile, p.split_k))
+        return;
+    if (wave == 0) {
+        A4 sum[RB][TB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                sum[rb][tb] = A4{0, 0, 0, 0};
+                for (int s = 0; s < p.split_k; ++s)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int t = SWAP ? m0 + tb * 16 + r16 : m0 + tb * 16 + 4 * g + v;
+                        const int n = SWAP ? n0 + rb * 16 + 4 * g + v : n0 + rb * 16 + r16;
+                        if (t < mend && n < p.N)
+                            sum[rb][tb][v] += ld_dev(part_ptr<FMT>(p, s, t, n));
+                    }
+            }
+        emit(sum);
+    }
+    rearm(p.counters + tile);
+}
+
+template <int FMT, bool SWAP, int TMS, int RB, int NW, int S, int CHK>
+hipError_t launch_stream_lds(const KArgs &a, dim3 grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((k_stream_lds<FMT, SWAP, TMS, RB, NW, S, CHK>), grid, dim3(64 * NW), 0, s, a);
+    return hipGetLastError();
+}
+
+#define QLIN_STREAM_LDS_INSTANCE(FMT, BIT, SW, TMS, RB, NW, S, CHK)                      \
+    {{QLIN_KERNEL_STREAM_LDS, SW, TMS, 16 * (RB), CHK, 1, NW, S, 1, 0}, BIT, FMT, SC_TC, \
+     &launch_stream_lds<FMT, (SW) != 0, TMS, RB, NW, S, CHK>}
+
+// (RB, NW, S, CHK) per token count TMS; LDS per workgroup is about
+// S * (16*RB + TMS) * CHK bytes.
+#define QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, TMS) \
+    X(FMT, BIT, SW, TMS, 1, 4, 2, 1024),            \
+    X(FMT, BIT, SW, TMS, 1, 8, 2, 1024),            \
+    X(FMT, BIT, SW, TMS, 1, 4, 4, 512),             \
+    X(FMT, BIT, SW, TMS, 1, 8, 3, 1024)
+
+#define QLIN_STREAM_LDS_SHAPES(X, FMT, BIT, SW)    \
+    QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 1),      \
+    QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 2),      \
+    QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 4),      \
+    QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 8),      \
+    QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 16),     \
+    QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 32),     \
+    X(FMT, BIT, SW, 16, 2, 4, 2, 1024),            \
+    X(FMT, BIT, SW, 32, 2, 8, 2, 1024)
+
+}  // namespace qlin

@@ -44,14 +44,14 @@ def candidates(fmt: str, M: int, N: int, K: int, max_split: int = 256):
     out = []
     KS = -(-K // 128)
     for base in q.instances_for(fmt):
-        if base.kernel == q.KERNEL_STREAM and -(-M // base.tile_m) > 4:
-            continue                      # the stream kernel is for small token counts
+        if base.kernel in (q.KERNEL_STREAM, q.KERNEL_STREAM_LDS) and -(-M // base.tile_m) > 4:
+            continue                      # the stream kernels are for small token counts
         if base.kernel == q.KERNEL_TILE and M < 32:
             continue
         split = 1
         while split <= min(max_split, 256):
             kw = base.waves_k if base.kernel == q.KERNEL_STREAM else 1
-            if split * kw > KS:
+            if split * kw > KS or (base.kernel == q.KERNEL_STREAM_LDS and split * 2 > KS):
                 break
             reds = (q.REDUCE_LAST_ARRIVER,) if split == 1 else (q.REDUCE_LAST_ARRIVER, q.REDUCE_TWO_PASS)
             for r in reds:
