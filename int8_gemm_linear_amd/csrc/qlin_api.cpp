@@ -227,6 +227,9 @@ qlin_config default_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
     return c;
 }
 
+qlin_status check_config(int fmt, int scal, int64_t M, int64_t N, int64_t K,
+                         const qlin_config &c, const Instance **inst);
+
 qlin_config select_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
 {
     ensure_table();
@@ -242,7 +245,9 @@ qlin_config select_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
     }
     if (!best)
         best = largest;
-    if (best)
+    // An entry that does not fit this M (or names an instance this build
+    // lacks) falls back to the built-in default rather than failing.
+    if (best && check_config(fmt, scal, M, N, K, best->cfg, nullptr) == QLIN_OK)
         return best->cfg;
     return default_config(fmt, scal, M, N, K);
 }

@@ -94,6 +94,23 @@ __device__ inline uint16_t bf16_bits(float f)
     return *reinterpret_cast<uint16_t *>(&h);
 }
 
+// Copy 16 bytes per lane HBM/L2 -> LDS (global_load_lds_dwordx4): lane i's
+// bytes land at lds + 16*i (the LDS base is wave-uniform, passed in M0).
+// Written as inline assembly on purpose: for the builtin the compiler must
+// assume the in-flight copy may alias any later LDS read and inserts
+// vmcnt(0) before every ds_read, which would also wait for the copies of
+// later pipeline stages.  Callers therefore wait for their own copies with
+// explicit, exactly counted s_waitcnt vmcnt(n) before reading the stage.
+// No register output: the copy writes only LDS.
+__device__ inline void lds_dma16(const void *g, const void *lds)
+{
+    const unsigned off = (unsigned)(size_t)lds;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(off))
+                 : "memory", "m0");
+}
+
 __device__ inline v4i ld_nt(const uint8_t *p)
 {
     return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));

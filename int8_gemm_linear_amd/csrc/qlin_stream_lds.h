@@ -115,9 +115,7 @@ k_stream_lds(KArgs p)
         for (int i = 0; i < L; ++i) {
             const int ins = wave + i * NW;
             if (slot * 16 < len)
-                __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void *)(src[i] + k0),
-                    (__attribute__((address_space(3))) void *)(st + ins * 1024), 16, 0, 0);
+                lds_dma16(src[i] + k0, st + ins * 1024);
         }
     };
 

@@ -3,11 +3,18 @@
 //
 // One workgroup computes a BM (tokens) x BN (weights) output tile of one K
 // split with WM x WN waves, each owning a (BM/WM) x (BN/WN) sub-tile of
-// 32x32 matrix-core blocks.  Per 128-byte K step both operand tiles are
-// copied HBM/L2 -> LDS with global_load_lds_dwordx4 (16 bytes per lane
-// written straight into LDS, no register staging), into a two-stage ring:
-// the copy of step s+1 is in flight while step s is read from LDS
-// (ds_read_b128) into the matrix cores.
+// 32x32 matrix-core blocks (accumulators live in the AGPR half of the
+// register file).  Per 128-byte K step both operand tiles are copied
+// HBM/L2 -> LDS with global_load_lds_dwordx4 (16 bytes per lane written
+// straight into LDS, no register staging) into a ring of S stages: while
+// step s is read from LDS (ds_read_b128) into the matrix cores, steps
+// s+1 .. s+S-1 are in flight.  Every global load inside the loop is one of
+// these copies (L per wave per step), so the wait for step s is an exact
+// s_waitcnt vmcnt(L * steps issued after s), and one barrier per step both
+// publishes step s and frees the stage step s+S-1 is copied into.  Within a
+// step the wave loads its B fragments once and the A fragments one 32-row
+// block at a time, issuing the MFMA pieces across the independent B blocks
+// so consecutive matrix-core instructions do not wait on each other.
 //
 // LDS layout of a stage: [BM rows of A][BN rows of B], 128 bytes per row.
 // The eight 16-byte chunks of row r are stored XOR-swizzled, chunk c at slot
@@ -29,7 +36,8 @@
 // columns to store.  Split-K is grid.z, as in the stream kernel.
 // Block_FP8 promotes each 128-wide K group into the running fp32 sum with
 // sA[t][g] * sB[n/128][g] (built with SWAP only, where each lane needs one
-// token scale per block and one weight-block scale per wave).
+// token scale per block and one weight-block scale per wave, and with S = 2:
+// the scales of step s+1 are loaded into registers next to its copy).
 #pragma once
 
 #include "qlin_device.h"
@@ -38,7 +46,40 @@ namespace qlin {
 
 __device__ inline int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int FMT, int SCAL, bool SWAP, int BM, int BN, int WM, int WN>
+template <int N>
+__device__ inline void wait_vm_tile()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    if constexpr (N == 0)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One MFMA piece of a 128-byte K step on a 32x32 block: int8 has four
+// pieces of 16 bytes (v_mfma_i32_32x32x32_i8), e4m3 two pieces of 32 bytes
+// (v_mfma_f32_32x32x64_f8f6f4).  Same operand layout as mma32.
+template <int FMT> struct Pieces;
+template <> struct Pieces<FMT_INT8> { static constexpr int n = 4; };
+template <> struct Pieces<FMT_E4M3> { static constexpr int n = 2; };
+
+template <int FMT>
+__device__ inline typename AccT<FMT>::v16 mma32_piece(const v4i *a, const v4i *b, int j,
+                                                      typename AccT<FMT>::v16 c);
+template <>
+__device__ inline v16i mma32_piece<FMT_INT8>(const v4i *a, const v4i *b, int j, v16i c)
+{
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a[j], b[j], c, 0, 0, 0);
+}
+template <>
+__device__ inline v16f mma32_piece<FMT_E4M3>(const v4i *a, const v4i *b, int j, v16f c)
+{
+    v8i x = __builtin_shufflevector(a[2 * j], a[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    v8i y = __builtin_shufflevector(b[2 * j], b[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 0, 0, 0);
+}
+
+template <int FMT, int SCAL, bool SWAP, int BM, int BN, int WM, int WN, int S>
 __global__ void __launch_bounds__(64 * WM * WN)
 k_tile(KArgs p)
 {
@@ -54,8 +95,10 @@ k_tile(KArgs p)
     constexpr int GM = 4;
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
     static_assert(ROWS % 8 == 0, "rows");
+    static_assert(S >= 2 && S <= 4, "stages");
+    static_assert(SCAL == SC_TC || S == 2, "block scaling keeps scales in a register double buffer");
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[S * STAGE];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -109,15 +152,17 @@ k_tile(KArgs p)
         src[i] = base + 16 * ((lane & 7) ^ lds_swz(r));
     }
 
+    static_assert(ROWS / 8 % NW == 0, "copies must split evenly over the waves");
+    constexpr int L = GPW + (SCAL == SC_BLOCK ? FM + FN : 0);   // loads per wave per step
+    static_assert(L * (S - 2) <= 63, "vmcnt range");
+
     auto issue = [&](int st, int stage) {
         uint8_t *dst0 = lds + stage * STAGE;
 #pragma unroll
         for (int i = 0; i < GPW; ++i) {
             const int grp_i = wave + i * NW;
             if (GROUPS % NW == 0 || grp_i < GROUPS)
-                __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void *)(src[i] + (int64_t)st * 128),
-                    (__attribute__((address_space(3))) void *)(dst0 + grp_i * 1024), 16, 0, 0);
+                lds_dma16(src[i] + (int64_t)st * 128, dst0 + grp_i * 1024);
         }
     };
 
@@ -150,12 +195,13 @@ k_tile(KArgs p)
     const int fr = lane & 31;          // fragment row
     const int fh = lane >> 5;          // 64-byte half of the K step
 
-    if (s_beg < s_end) {
-        issue(s_beg, 0);
-        load_scales(s_beg);
+    const int nst = s_end - s_beg;
+    for (int i = 0; i < S - 1 && i < nst; ++i) {
+        issue(s_beg + i, i);
+        load_scales(s_beg + i);
     }
-    for (int s = s_beg; s < s_end; ++s) {
-        const int stage = (s - s_beg) & 1;
+    for (int i = 0; i < nst; ++i) {
+        const int s = s_beg + i;
         float sa[FM], sb[FN];
         if constexpr (SCAL == SC_BLOCK) {
 #pragma unroll
@@ -163,13 +209,19 @@ k_tile(KArgs p)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) sb[fn] = sb_next[fn];
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const int after = min(S - 2, nst - 1 - i);      // steps issued after step i
+        if (after >= 2)
+            wait_vm_tile<L * 2>();
+        else if (after == 1)
+            wait_vm_tile<L>();
+        else
+            wait_vm_tile<0>();
         __syncthreads();
-        if (s + 1 < s_end) {
-            issue(s + 1, stage ^ 1);
-            load_scales(s + 1);
+        if (i + S - 1 < nst) {
+            issue(s + S - 1, (i + S - 1) % S);
+            load_scales(s + S - 1);
         }
-        const uint8_t *la = lds + stage * STAGE;
+        const uint8_t *la = lds + (i % S) * STAGE;
         const uint8_t *lb = la + BM * 128;
         v4i bf[FN][4];
 #pragma unroll
@@ -181,18 +233,23 @@ k_tile(KArgs p)
             for (int j = 0; j < 4; ++j)
                 bf[fn][j] = *reinterpret_cast<const v4i *>(rowp + 16 * ((4 * fh + j) ^ sw));
         }
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            v4i af[4];
+        // A fragments one 32-row block at a time, double-buffered: block fm+1
+        // is read from LDS while block fm's MFMA pieces issue (interleaved
+        // across the FN independent accumulators).  The scheduling barriers
+        // keep the compiler from hoisting every read, which would not fit
+        // the register file at 8 waves per workgroup.
+        auto load_a = [&](v4i (&af)[4], int fm) {
             const int r = wm * WTM + fm * 32 + fr;
             const uint8_t *rowp = la + r * 128;
             const int sw = lds_swz(r);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 af[j] = *reinterpret_cast<const v4i *>(rowp + 16 * ((4 * fh + j) ^ sw));
+        };
+        auto block = [&](const v4i (&af)[4], int fm) {
+            if constexpr (SCAL == SC_BLOCK) {
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                if constexpr (SCAL == SC_BLOCK) {
+                for (int fn = 0; fn < FN; ++fn) {
                     A16 z;
 #pragma unroll
                     for (int v = 0; v < 16; ++v) z[v] = 0;
@@ -201,10 +258,31 @@ k_tile(KArgs p)
 #pragma unroll
                     for (int v = 0; v < 16; ++v)
                         acc[fm][fn][v] = __builtin_fmaf((float)pz[v], scale, (float)acc[fm][fn][v]);
-                } else {
-                    acc[fm][fn] = SWAP ? mma32<FMT>(bf[fn], af, acc[fm][fn])
-                                       : mma32<FMT>(af, bf[fn], acc[fm][fn]);
                 }
+            } else {
+#pragma unroll
+                for (int j = 0; j < Pieces<FMT>::n; ++j)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+                        acc[fm][fn] = SWAP ? mma32_piece<FMT>(bf[fn], af, j, acc[fm][fn])
+                                           : mma32_piece<FMT>(af, bf[fn], j, acc[fm][fn]);
+            }
+        };
+        v4i a0[4], a1[4];
+        load_a(a0, 0);
+#pragma unroll
+        for (int fm = 0; fm < FM; fm += 2) {
+            if (fm + 1 < FM)
+                load_a(a1, fm + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            block(a0, fm);
+            __builtin_amdgcn_sched_barrier(0);
+            if (fm + 1 < FM) {
+                if (fm + 2 < FM)
+                    load_a(a0, fm + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                block(a1, fm + 1);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -307,23 +385,35 @@ k_tile(KArgs p)
     rearm(p.counters + tile);
 }
 
-template <int FMT, int SCAL, bool SWAP, int BM, int BN, int WM, int WN>
+template <int FMT, int SCAL, bool SWAP, int BM, int BN, int WM, int WN, int S>
 hipError_t launch_tile(const KArgs &a, dim3 grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_tile<FMT, SCAL, SWAP, BM, BN, WM, WN>), grid, dim3(64 * WM * WN), 0, s,
+    hipLaunchKernelGGL((k_tile<FMT, SCAL, SWAP, BM, BN, WM, WN, S>), grid, dim3(64 * WM * WN), 0, s,
                        a);
     return hipGetLastError();
 }
 
-#define QLIN_TILE_INSTANCE(FMT, SCAL, BIT, SW, BM, BN, WM, WN)                                \
-    {{QLIN_KERNEL_TILE, SW, BM, BN, 128, WM, WN, 2, 1, 0}, BIT, FMT, SCAL,                    \
-     &launch_tile<FMT, SCAL, (SW) != 0, BM, BN, WM, WN>}
+#define QLIN_TILE_INSTANCE(FMT, SCAL, BIT, SW, BM, BN, WM, WN, S)                             \
+    {{QLIN_KERNEL_TILE, SW, BM, BN, 128, WM, WN, S, 1, 0}, BIT, FMT, SCAL,                    \
+     &launch_tile<FMT, SCAL, (SW) != 0, BM, BN, WM, WN, S>}
 
-// (BM, BN, WM, WN) shapes shared by the formats.
+// (BM, BN, WM, WN, S) for token/channel scaling; LDS = S * (BM + BN) * 128 B.
 #define QLIN_TILE_SHAPES(X, FMT, SCAL, BIT, SW) \
-    X(FMT, SCAL, BIT, SW, 64, 128, 1, 4),       \
-    X(FMT, SCAL, BIT, SW, 128, 128, 2, 2),      \
-    X(FMT, SCAL, BIT, SW, 128, 256, 2, 2),      \
-    X(FMT, SCAL, BIT, SW, 256, 128, 2, 2)
+    X(FMT, SCAL, BIT, SW, 64, 128, 1, 4, 4),    \
+    X(FMT, SCAL, BIT, SW, 128, 128, 2, 2, 2),   \
+    X(FMT, SCAL, BIT, SW, 128, 128, 2, 2, 4),   \
+    X(FMT, SCAL, BIT, SW, 128, 256, 2, 2, 3),   \
+    X(FMT, SCAL, BIT, SW, 256, 128, 2, 2, 3),   \
+    X(FMT, SCAL, BIT, SW, 256, 256, 2, 4, 2),   \
+    X(FMT, SCAL, BIT, SW, 256, 256, 4, 2, 2),   \
+    X(FMT, SCAL, BIT, SW, 256, 128, 4, 2, 3),   \
+    X(FMT, SCAL, BIT, SW, 128, 256, 2, 4, 3)
+
+// Block scaling: S = 2.
+#define QLIN_TILE_SHAPES_BLOCK(X, FMT, SCAL, BIT, SW) \
+    X(FMT, SCAL, BIT, SW, 64, 128, 1, 4, 2),          \
+    X(FMT, SCAL, BIT, SW, 128, 128, 2, 2, 2),         \
+    X(FMT, SCAL, BIT, SW, 128, 256, 2, 2, 2),         \
+    X(FMT, SCAL, BIT, SW, 256, 128, 2, 2, 2)
 
 }  // namespace qlin

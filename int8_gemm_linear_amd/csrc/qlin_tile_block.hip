@@ -3,7 +3,7 @@
 
 namespace qlin {
 
-static const Instance kInstances[] = {QLIN_TILE_SHAPES(QLIN_TILE_INSTANCE, FMT_E4M3, SC_BLOCK, FB_BLOCK, 1)};
+static const Instance kInstances[] = {QLIN_TILE_SHAPES_BLOCK(QLIN_TILE_INSTANCE, FMT_E4M3, SC_BLOCK, FB_BLOCK, 1)};
 
 const Instance *tile_instances_block(int *count)
 {

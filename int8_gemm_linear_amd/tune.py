@@ -113,10 +113,21 @@ class Point:
 
 
 def agree(fmt, y, ref) -> bool:
+    """Sanity check of a candidate against the reference candidate (parity
+    itself is established by the tests against the oracle).  INT8: bit for
+    bit.  FP8: accumulation order differs between candidates, so compare
+    normwise and against the output's scale, not elementwise-relative
+    (outputs near a cancellation have no meaningful relative error)."""
     if fmt == "int8":
         return torch.equal(y.view(torch.int16), ref.view(torch.int16))
-    d = (y.float() - ref.float()).abs()
-    return bool((d <= ref.float().abs() * 2.0 ** -6 + 1e-30).all() or d.max().item() == 0)
+    yf, rf = y.float(), ref.float()
+    if not torch.isfinite(yf).all():
+        return False
+    d = (yf - rf).abs()
+    scale = rf.abs().max().item()
+    nrm = torch.linalg.vector_norm(rf).item()
+    return bool(d.max().item() <= 2.0 ** -5 * scale
+                and (torch.linalg.vector_norm(yf - rf).item() <= 1e-2 * nrm or nrm == 0))
 
 
 def tune_point(fmt, M, N, K, log=None, done=None, max_cands=None, verbose=False):
@@ -167,6 +178,8 @@ def main():
     ap.add_argument("--table", default=None, help="write/merge the best configs into this table")
     ap.add_argument("--max-cands", type=int, default=None)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--min-m", type=int, default=0)
+    ap.add_argument("--max-m", type=int, default=1 << 30)
     args = ap.parse_args()
     sys.path.insert(0, ROOT)
     import synth
@@ -177,6 +190,7 @@ def main():
     for p in args.point:
         f, M, N, K = p.split(",")
         points.append((f, int(M), int(N), int(K)))
+    points = [pt for pt in points if args.min_m <= pt[1] <= args.max_m]
     done = {}
     if args.jsonl and os.path.exists(args.jsonl):
         for ln in open(args.jsonl):

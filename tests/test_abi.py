@@ -176,3 +176,19 @@ def test_status_strings():
     lib = q.lib()
     for s in range(10):
         assert lib.qlin_status_string(s)
+
+
+def test_compiled_in_table_entries_are_valid():
+    """Every entry of the shipped table names a built instance valid for its own shape."""
+    path = os.path.join(ROOT, "int8_gemm_linear_amd", "configs", "qlin_mi355x.cfg")
+    n = 0
+    for ln in open(path):
+        f = ln.split("#")[0].split()
+        if not f:
+            continue
+        fmt, N, K, M = f[0], int(f[1]), int(f[2]), int(f[3])
+        c = q.Config(*[int(x) for x in f[4:14]])
+        assert q.check_config(fmt, M, N, K, c) == 0, ln
+        assert q.select_config(fmt, M, N, K) == c, ln
+        n += 1
+    assert n == q.config_table_size()
