@@ -1,0 +1,186 @@
+"""Text summaries of rocprofv3 output (kernel traces and HBM byte counters).
+
+Kernel trace (a rocprofv3 --kernel-trace output folder, csv or rocpd database):
+
+    python -m int8_gemm_linear_amd.profsum trace <dir>
+
+HBM traffic per GEMM call, from two counter runs of the same bench command,
+one with ``--pmc FETCH_SIZE`` and one with ``--pmc WRITE_SIZE`` (csv output),
+each run also holding one plain copy of known size (``bench.py --copy-calib``)
+that calibrates the counter to bytes:
+
+    python -m int8_gemm_linear_amd.profsum traffic --fetch <dir> --write <dir> \
+        --workload int8_1p7b_decode --out profiles/<name>.json
+
+The traffic record carries a fingerprint of the kernel sources and the config
+table, so a reader can tell whether the kernels have changed since the
+counters were taken.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sqlite3
+import sys
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 256 << 20          # the calibration copy of bench.py --copy-calib
+COPY_TAG = "bitwise_not"        # its kernel is torch's elementwise bitwise_not
+
+
+def fingerprint(table_path: str | None = None) -> str:
+    """sha256 over the kernel sources and the config table in use."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    tp = table_path or os.path.join(PKG, "configs", "qlin_mi355x.cfg")
+    with open(tp, "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _is_gemm(name: str) -> bool:
+    return "qlin::k_stream" in name or "qlin::k_tile" in name
+
+
+def _is_qlin(name: str) -> bool:
+    return "qlin::" in name
+
+
+def kernel_durations(folder: str) -> dict[str, list[float]]:
+    """{kernel name: [duration ns, ...]} from a kernel-trace folder."""
+    out: dict[str, list[float]] = collections.OrderedDict()
+    csvs = glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True)
+    if csvs:
+        for p in csvs:
+            with open(p, newline="") as f:
+                for r in csv.DictReader(f):
+                    d = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+                    out.setdefault(r["Kernel_Name"], []).append(d)
+        return out
+    dbs = glob.glob(os.path.join(folder, "**", "*.db"), recursive=True)
+    if not dbs:
+        raise SystemExit(f"no kernel trace under {folder}")
+    for p in dbs:
+        db = sqlite3.connect(p)
+        for name, d in db.execute("select name, duration from kernels"):
+            out.setdefault(name, []).append(float(d))
+    return out
+
+
+def trace_summary(folder: str) -> str:
+    agg = kernel_durations(folder)
+    lines = [f"{'calls':>6} {'avg_us':>9} {'min_us':>8} {'max_us':>8} {'total_ms':>9}  kernel"]
+    for name, ds in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        d = np.array(ds) / 1e3
+        lines.append(f"{len(d):6d} {d.mean():9.3f} {d.min():8.3f} {d.max():8.3f} "
+                     f"{d.sum() / 1e3:9.3f}  {name[:110]}")
+    gemm = [k for k in agg if _is_gemm(k)]
+    red = [k for k in agg if "qlin::k_reduce" in k]
+    if gemm:
+        g = np.concatenate([np.array(agg[k]) for k in gemm]) / 1e3
+        tot = (g.sum() + sum(sum(agg[k]) for k in red) / 1e3)
+        lines.append("")
+        lines.append(f"GEMM kernels: {len(g)} launches, mean {g.mean():.3f} us/launch")
+        lines.append(f"per GEMM call (GEMM kernel + its split-K reduce when two-pass): "
+                     f"{tot / len(g):.3f} us/call")
+    return "\n".join(lines)
+
+
+def counter_values(folder: str, counter: str, with_grid: bool = False):
+    """[(kernel name, value)] per dispatch, in dispatch order, from a --pmc csv
+    run; with_grid adds the dispatch's grid size as a third field."""
+    rows = []
+    paths = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    per = collections.OrderedDict()
+    for p in paths:
+        with open(p, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                key = (p, int(r["Dispatch_Id"]))
+                grid = "x".join(r[k] for k in sorted(r) if k and k.startswith("Grid_Size"))
+                name, v, _ = per.get(key, (r["Kernel_Name"], 0.0, grid))
+                per[key] = (name, v + float(r["Counter_Value"]), grid)
+    for key in sorted(per, key=lambda k: (k[0], k[1])):
+        rows.append(per[key] if with_grid else per[key][:2])
+    return rows
+
+
+def per_launch_table(folder: str, counter: str, factor: float) -> str:
+    """Mean calibrated bytes per dispatch of every (qlin kernel, grid) pair."""
+    agg = collections.OrderedDict()
+    for n, v, g in counter_values(folder, counter, with_grid=True):
+        if _is_qlin(n):
+            agg.setdefault((n, g), []).append(v * 1024.0 * factor)
+    lines = [f"{'calls':>6} {'mean_MB':>9} {'min_MB':>9} {'max_MB':>9}  grid  kernel"]
+    for (n, g), vs in agg.items():
+        a = np.array(vs) / 1e6
+        lines.append(f"{len(a):6d} {a.mean():9.3f} {a.min():9.3f} {a.max():9.3f}  {g}  {n[:90]}")
+    return "\n".join(lines)
+
+
+def traffic(fetch_dir: str, write_dir: str, workload: str, table: str | None) -> dict:
+    out = {"workload": workload, "fingerprint": fingerprint(table)}
+    for tag, folder, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        vals = counter_values(folder, counter)
+        copy = [v for n, v in vals if COPY_TAG in n]
+        if len(copy) != 1:
+            raise SystemExit(f"{counter}: expected one calibration copy, found {len(copy)}")
+        factor = COPY_BYTES / (copy[0] * 1024.0)
+        calls = [v for n, v in vals if _is_gemm(n)]
+        qlin = [v for n, v in vals if _is_qlin(n)]
+        if not calls:
+            raise SystemExit(f"{counter}: no GEMM dispatches")
+        per_call = sum(qlin) * 1024.0 * factor / len(calls)
+        out[tag] = {"counter": counter, "calib_copy_kib": copy[0], "factor": round(factor, 5),
+                    "gemm_calls": len(calls), "bytes_per_call": round(per_call, 1)}
+    out["traffic_bytes_per_call"] = round(out["fetch"]["bytes_per_call"] + out["write"]["bytes_per_call"], 1)
+    return out
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("folder")
+    c = sub.add_parser("traffic")
+    c.add_argument("--fetch", required=True)
+    c.add_argument("--write", required=True)
+    c.add_argument("--workload", required=True)
+    c.add_argument("--table", default=None)
+    c.add_argument("--alg-bytes-per-call", type=float, default=None)
+    c.add_argument("--out", default=None)
+    c.add_argument("--per-launch", action="store_true", help="also print per (kernel, grid) means")
+    a = ap.parse_args(argv)
+    if a.cmd == "trace":
+        print(trace_summary(a.folder))
+        return
+    rec = traffic(a.fetch, a.write, a.workload, a.table)
+    if a.alg_bytes_per_call:
+        rec["alg_bytes_per_call"] = a.alg_bytes_per_call
+        rec["traffic_over_alg"] = round(rec["traffic_bytes_per_call"] / a.alg_bytes_per_call, 4)
+    if a.per_launch:
+        for tag, folder in (("fetch", a.fetch), ("write", a.write)):
+            print(f"== {rec[tag]['counter']} (calibrated)")
+            print(per_launch_table(folder, rec[tag]["counter"], rec[tag]["factor"]))
+    s = json.dumps(rec, indent=1)
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(s + "\n")
+    print(s)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
