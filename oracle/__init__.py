@@ -71,6 +71,12 @@ def _load():
     lib.orc_e4m3_decode_n.argtypes = [P, P, I64]
     lib.orc_double_to_bf16_n.restype = None
     lib.orc_double_to_bf16_n.argtypes = [P, P, I64]
+    lib.orc_e4m3_nearest.restype = ctypes.c_uint8
+    lib.orc_e4m3_nearest.argtypes = [ctypes.c_float]
+    lib.orc_quant_per_token.restype = I
+    lib.orc_quant_per_token.argtypes = [I, I64, I64, P, I64, P, I64, P]
+    lib.orc_quant_per_group.restype = I
+    lib.orc_quant_per_group.argtypes = [I64, I64, I64, P, I64, P, I64, P]
     _lib = lib
     return lib
 
@@ -186,3 +192,47 @@ def scaled_mm_points(fmt: int, A, sA, B, sB, ms, ns, *, block: bool = False,
     if rc != 0:
         raise RuntimeError("oracle rejected its arguments")
     return Result(Y, ydbl, bound, acc_i if acc_i is not None else acc_f)
+
+
+def _bf16_bits(x) -> np.ndarray:
+    """bf16 input as its bit patterns: accepts uint16 bits or float32 values
+    that are exactly bf16 (the low 16 bits must be zero)."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return np.ascontiguousarray(x)
+    f = np.ascontiguousarray(x, np.float32).view(np.uint32)
+    if np.any(f & 0xFFFF):
+        raise ValueError("input values are not bfloat16")
+    return (f >> 16).astype(np.uint16)
+
+
+def e4m3_nearest(v: float) -> int:
+    """Nearest OCP e4m3 code to an fp32 value in [-448, 448], ties to even."""
+    return int(_load().orc_e4m3_nearest(float(v)))
+
+
+def quant_per_token(x, fmt: int):
+    """Dynamic per-token quantization of a bf16 activation [M,K]:
+    (codes uint8 [M,K], scales fp32 [M]), scale = amax/448 (e4m3) or
+    amax/127 (int8), codes = nearest-even of x/scale, clamped."""
+    xb = _bf16_bits(x)
+    M, K = xb.shape
+    q = np.zeros((M, K), np.uint8)
+    s = np.zeros(M, np.float32)
+    if _load().orc_quant_per_token(fmt, M, K, xb.ctypes.data, K, q.ctypes.data, K,
+                                   s.ctypes.data) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return q, s
+
+
+def quant_per_group(x, group: int = 128):
+    """Per-token-group e4m3 quantization of a bf16 activation [M,K]:
+    (codes uint8 [M,K], scales fp32 [M, K/group])."""
+    xb = _bf16_bits(x)
+    M, K = xb.shape
+    q = np.zeros((M, K), np.uint8)
+    s = np.zeros((M, K // group), np.float32)
+    if _load().orc_quant_per_group(M, K, group, xb.ctypes.data, K, q.ctypes.data, K,
+                                   s.ctypes.data) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return q, s

@@ -306,3 +306,111 @@ void orc_double_to_bf16_n(const double *in, uint16_t *out, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = orc_double_to_bf16(in[i]);
 }
+
+/* ---------------------------------------------------------------------- */
+/* Activation quantization (the step upstream of the GEMM).               */
+/* ---------------------------------------------------------------------- */
+/*
+ * "HelionがvLLMに統合 ..." (24-ai.news), section "vLLMに統合されたカーネル"
+ * (kernels integrated into vLLM), items 1 and 5: dynamic per-token FP8
+ * quantization and per-token-group FP8 quantization of the activations
+ * feeding scaled_mm / scaled_mm_blockwise.  The pages give names only.
+ * Readings (listed in the design doc): the input is bfloat16; a row (or 1x128
+ * group) gets scale s = amax / 448 (e4m3) or amax / 127 (int8), computed in
+ * fp32 with one correctly rounded division; an all-zero row or group gets
+ * s = 1; each code is the quotient x / s (fp32, correctly rounded) clamped
+ * to +-448 and rounded to the nearest e4m3 value, ties to the even code
+ * (int8: rounded to the nearest integer, ties to even, clamped to +-127).
+ *
+ * The fp32 steps are taken in C float arithmetic (x86-64 SSE: every float
+ * operation is rounded once to fp32; built with -ffp-contract=off).  The
+ * e4m3 rounding is done by exhaustive search over the 127 non-negative
+ * finite codes, decoded by orc_e4m3_to_double: the nearest value wins and
+ * a tie goes to the code whose last mantissa bit is 0.
+ */
+
+static float orc_bf16_to_float(uint16_t h)
+{
+    uint32_t b = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &b, sizeof f);
+    return f;
+}
+
+/* Nearest e4m3 code to v (|v| <= 448), ties to the even code; the sign of
+ * v (including -0) is kept. */
+uint8_t orc_e4m3_nearest(float v)
+{
+    double a = fabs((double)v);
+    int best = 0;
+    double best_d = a;                     /* distance to code 0 (+0) */
+    for (int c = 1; c <= 0x7E; ++c) {
+        double d = fabs(orc_e4m3_to_double((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(best | (signbit(v) ? 0x80 : 0));
+}
+
+/* Round half to even on a float holding a value of magnitude < 2^23. */
+static float orc_rint_even(float x)
+{
+    float f = floorf(x);
+    float r = x - f;                       /* exact: x and f share the binade scale */
+    if (r > 0.5f || (r == 0.5f && fmodf(f, 2.0f) != 0.0f))
+        f += 1.0f;
+    return f;
+}
+
+static void orc_quant_span(int fmt, const uint16_t *x, int64_t n, uint8_t *q, float *s_out)
+{
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = fabsf(orc_bf16_to_float(x[i]));
+        if (a > amax) amax = a;
+    }
+    const float qmax = fmt == ORC_FMT_INT8 ? 127.0f : 448.0f;
+    float s = amax / qmax;
+    if (amax == 0.0f) s = 1.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float v = orc_bf16_to_float(x[i]) / s;
+        if (fmt == ORC_FMT_INT8) {
+            float r = orc_rint_even(v);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            q[i] = (uint8_t)(int8_t)r;
+        } else {
+            if (v > 448.0f) v = 448.0f;
+            if (v < -448.0f) v = -448.0f;
+            q[i] = orc_e4m3_nearest(v);
+        }
+    }
+    *s_out = s;
+}
+
+/* Per-token: x [M, ldx] bf16 bits -> q [M, ldq] codes, s [M]. */
+int orc_quant_per_token(int fmt, int64_t M, int64_t K, const uint16_t *x, int64_t ldx,
+                        uint8_t *q, int64_t ldq, float *s)
+{
+    if ((fmt != ORC_FMT_E4M3 && fmt != ORC_FMT_INT8) || M < 0 || K < 0 || ldx < K || ldq < K)
+        return 1;
+    for (int64_t m = 0; m < M; ++m)
+        orc_quant_span(fmt, x + m * ldx, K, q + m * ldq, s + m);
+    return 0;
+}
+
+/* Per 1 x group along K (e4m3): s [M, K/group] row-major. */
+int orc_quant_per_group(int64_t M, int64_t K, int64_t group, const uint16_t *x, int64_t ldx,
+                        uint8_t *q, int64_t ldq, float *s)
+{
+    if (M < 0 || K < 0 || group <= 0 || K % group || ldx < K || ldq < K)
+        return 1;
+    const int64_t G = K / group;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t g = 0; g < G; ++g)
+            orc_quant_span(ORC_FMT_E4M3, x + m * ldx + g * group, group,
+                           q + m * ldq + g * group, s + m * G + g);
+    return 0;
+}
