@@ -173,6 +173,7 @@ def cpu_baseline(wl: Workload, threads: int, budget_s: float):
     from tests import parity as par
 
     done_bytes = 0
+    done_flops = 0
     n_calls = 0
     first = []
     t0 = time.perf_counter()
@@ -182,6 +183,7 @@ def cpu_baseline(wl: Workload, threads: int, budget_s: float):
             ref = oracle.scaled_mm(par.FMT_CODE[case.fmt], case.A, case.sA, case.B, case.sB,
                                    block=case.block, nthreads=threads)
             done_bytes += it["bytes"]
+            done_flops += it["flops"]
             n_calls += 1
             if len(first) < len(wl.items):
                 first.append((it, ref))
@@ -190,7 +192,31 @@ def cpu_baseline(wl: Workload, threads: int, budget_s: float):
         if time.perf_counter() - t0 > budget_s:
             break
     secs = time.perf_counter() - t0
-    return done_bytes, secs, n_calls, first
+    return done_bytes, done_flops, secs, n_calls, first
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def dispatch_cost():
+    """Host-side dispatch cost of the C ABI (int8_gemm_linear_amd/qlin_dispatch_bench,
+    built with the library): one JSON object, or None when it is not built."""
+    import subprocess
+    exe = os.path.join(ROOT, "int8_gemm_linear_amd", "qlin_dispatch_bench")
+    if not os.path.exists(exe):
+        return None
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        log("dispatch bench failed:", r.stderr[-300:])
+        return None
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 def load_traffic(workload: str, table: str | None):
@@ -220,6 +246,7 @@ def main():
                     help="also run one 256 MiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--table", default=None, help="config table file to load before running")
     ap.add_argument("--per-point", action="store_true", help="print per-point timings to stderr")
+    ap.add_argument("--no-dispatch", action="store_true", help="skip the host dispatch-cost run")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -269,7 +296,7 @@ def main():
     if not args.no_cpu:
         from tests import parity as par
         threads = max(1, min(16, os.cpu_count() or 1))
-        done_bytes, secs, n_calls, first = cpu_baseline(wl, threads, args.cpu_budget)
+        done_bytes, done_flops, secs, n_calls, first = cpu_baseline(wl, threads, args.cpu_budget)
         # the GPU outputs of the last replayed step vs the oracle
         parity_ok = True
         for it, ref in first:
@@ -278,11 +305,18 @@ def main():
             except AssertionError as e:
                 parity_ok = False
                 log("PARITY FAIL", it["fmt"], it["M"], it["N"], it["K"], str(e)[:200])
+        b1, _, s1, n1, _ = cpu_baseline(wl, 1, args.cpu_budget / 3)
         cpu = {"value": done_bytes / secs / 1e12, "unit": "TB/s", "cores": threads,
                "kind": "oracle",
                "sample": f"{n_calls} GEMM calls ({n_calls / len(wl.items):.1f} passes over the "
                          f"{len(wl.items)} GEMMs of the workload, whole GEMMs), {secs:.1f} s on "
-                         f"{threads} threads (plain C, double/int64 accumulate)"}
+                         f"{threads} threads (plain C, double/int64 accumulate)",
+               "single_thread_value": b1 / s1 / 1e12,
+               "single_thread_sample": f"{n1} GEMM calls, {s1:.1f} s on 1 thread",
+               "gflops": round(done_flops / secs / 1e9, 2),
+               "host_cpu": cpu_model()}
+
+    dispatch = None if args.no_dispatch else dispatch_cost()
 
     flops_tops = wl.flops_per_step / (ms_step * 1e-3) / 1e12
     out = {
@@ -313,6 +347,7 @@ def main():
                      "isolated_launch_avg_us": round(kern_us / len(per_us), 3),
                      "traffic_src": traffic_src},
         "cpu_baseline": cpu,
+        "dispatch": dispatch,
         "parity_vs_oracle": parity_ok,
     }
     print(json.dumps(out), flush=True)

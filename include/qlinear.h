@@ -121,10 +121,12 @@ typedef enum qlin_reduce {
  * tile_m / tile_n as for STREAM, tile_k = bytes per row per LDS chunk (512
  * or 1024), waves_k waves share each chunk's K steps, stages = ring depth.
  * For the TILE kernel:
- * tile_m x tile_n output tile, tile_k = 128, waves_n x waves_k is the wave
- * grid over the tile (rows x columns).  split_k is 1..256, a power of two;
- * each split covers a contiguous, 128-aligned K range.  stages is the
- * pipeline depth (2). */
+ * tile_m x tile_n output tile, waves_n x waves_k is the wave grid over the
+ * tile (rows x columns), stages = depth of the LDS ring; tile_k = 128 is the
+ * ring of whole 128-byte K steps (all three formats), tile_k = 64 the ring of
+ * 64-byte half-steps with fragments prefetched into registers (token/channel
+ * scaling only).  split_k is 1..256, a power of two; each split covers a
+ * contiguous, 128-aligned K range. */
 typedef struct qlin_config {
     int32_t kernel;     /* qlin_kernel */
     int32_t variant;    /* qlin_variant */
@@ -175,6 +177,31 @@ qlin_status qlin_int8_accumulate(int64_t M, int64_t N, int64_t K,
                                  int32_t *acc, int64_t ldacc,
                                  void *workspace, size_t workspace_bytes, void *stream,
                                  const qlin_config *cfg);
+
+/* Activation quantization, the producer of A: dynamic per-token FP8 and
+ * per-token-group FP8 quantization, items 1 and 5 of the kernel list in
+ * "HelionがvLLMに統合 ..." (24-ai.news), section "vLLMに統合されたカーネル".
+ *
+ * X [M][ldx] bf16 bit patterns (row-major, K used per row) -> Q [M][ldq]
+ * codes (e4m3 or int8 bytes) and fp32 scales, such that X ~= Q * scale.
+ * Scale of a row (per token) or of a 1x128 group: amax / 448 (e4m3) or
+ * amax / 127 (int8), one correctly rounded fp32 division, 1 when amax = 0.
+ * Code: x / scale in fp32 (correctly rounded), clamped to +-448 and rounded
+ * to the nearest e4m3 value, ties to even (int8: nearest integer, ties to
+ * even, clamped to +-127).  The outputs feed qlin_scaled_mm /
+ * qlin_block_scaled_mm as A and a_scale.
+ *
+ * Shapes: M >= 0 (0 is a no-op), 0 < K <= 2^20, K % 16 == 0 (per group:
+ * K % 128 == 0).  ldx >= K with ldx % 8 == 0 (elements), ldq >= K with
+ * ldq % 16 == 0 (bytes); X and Q 16-byte aligned, scale 4-byte aligned.
+ * scale: [M] per token; [M][K/128] row-major per group.  The caller owns
+ * every buffer; the call is asynchronous on `stream` (a hipStream_t) and
+ * allocates nothing.  Errors as for qlin_scaled_mm. */
+qlin_status qlin_quant_per_token(qlin_dtype dt, int64_t M, int64_t K,
+                                 const uint16_t *X, int64_t ldx, void *Q, int64_t ldq,
+                                 float *scale, void *stream);
+qlin_status qlin_quant_per_group128(int64_t M, int64_t K, const uint16_t *X, int64_t ldx,
+                                    void *Q, int64_t ldq, float *scale, void *stream);
 
 /* The config the table selects for a problem: the entry for (scaling, dt,
  * N, K) at the smallest tuned M >= M (else the largest tuned M); shapes not

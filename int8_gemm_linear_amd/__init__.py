@@ -131,6 +131,10 @@ def _lib():
     lib.qlin_status_string.restype = ctypes.c_char_p
     lib.qlin_abi_version.argtypes = []
     lib.qlin_abi_version.restype = ctypes.c_int32
+    lib.qlin_quant_per_token.argtypes = [I, I64, I64, P, I64, P, I64, P, P]
+    lib.qlin_quant_per_token.restype = I
+    lib.qlin_quant_per_group128.argtypes = [I64, I64, P, I64, P, I64, P, P]
+    lib.qlin_quant_per_group128.restype = I
     _LIB = lib
     return lib
 
@@ -226,6 +230,55 @@ def scaled_mm(a_q, a_scale, b_q, b_scale, out=None, config: Config | None = None
     else:
         _call(_lib().qlin_scaled_mm_cfg, args + [ctypes.byref(c)], "qlin_scaled_mm_cfg")
     return out
+
+
+def _bf16_rows(x: torch.Tensor, name: str) -> int:
+    if x.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {x.dtype}")
+    return _rows(x, name)
+
+
+def quant_per_token(x, dtype=torch.float8_e4m3fn, out=None, scale=None):
+    """Dynamic per-token quantization of bf16 activations x [M,K]: returns
+    (codes [M,K] of `dtype` (float8_e4m3fn or int8), scales float32 [M]),
+    scale = amax/448 (e4m3) or amax/127 (int8), codes = nearest-even of
+    x/scale, clamped.  The outputs are scaled_mm's a_q and a_scale."""
+    ldx = _bf16_rows(x, "x")
+    M, K = x.shape
+    dt = E4M3 if dtype == torch.float8_e4m3fn else (INT8 if dtype == torch.int8 else None)
+    if dt is None:
+        raise TypeError("dtype must be float8_e4m3fn or int8")
+    if out is None:
+        out = torch.empty((M, K), dtype=dtype, device=x.device)
+    elif out.dtype != dtype or tuple(out.shape) != (M, K) or out.stride(1) != 1:
+        raise ValueError("out must be a [M,K] tensor of dtype with contiguous rows")
+    if scale is None:
+        scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _scale(scale, (M,), "scale")
+    stream = torch.cuda.current_stream(x.device)
+    _call(_lib().qlin_quant_per_token, [dt, M, K, x.data_ptr(), ldx, out.data_ptr(), out.stride(0),
+                                        scale.data_ptr(), stream.cuda_stream], "qlin_quant_per_token")
+    return out, scale
+
+
+def quant_per_group128(x, out=None, scale=None):
+    """Per-token-group (1x128) e4m3 quantization of bf16 activations x [M,K]:
+    returns (codes float8_e4m3fn [M,K], scales float32 [M, K/128]), the
+    a_q and a_scale of block_scaled_mm."""
+    ldx = _bf16_rows(x, "x")
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=x.device)
+    elif out.dtype != torch.float8_e4m3fn or tuple(out.shape) != (M, K) or out.stride(1) != 1:
+        raise ValueError("out must be a float8_e4m3fn [M,K] tensor with contiguous rows")
+    if scale is None:
+        scale = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    _scale(scale, (M, K // 128), "scale")
+    stream = torch.cuda.current_stream(x.device)
+    _call(_lib().qlin_quant_per_group128, [M, K, x.data_ptr(), ldx, out.data_ptr(), out.stride(0),
+                                           scale.data_ptr(), stream.cuda_stream],
+          "qlin_quant_per_group128")
+    return out, scale
 
 
 def block_scaled_mm(a_q, a_scale, b_q, b_scale, out=None, config: Config | None = None,

@@ -16,15 +16,19 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqlinear.so")
+DISPATCH_BENCH = os.path.join(PKG, "qlin_dispatch_bench")
 TABLE = os.path.join(PKG, "configs", "qlin_mi355x.cfg")
 
 SOURCES = [
     "qlin_api.cpp",
     "qlin_reduce.hip",
+    "qlin_quant.hip",
     "qlin_stream_fp8.hip",
     "qlin_stream_int8.hip",
     "qlin_stream_block.hip",
     "qlin_tile_fp8.hip",
+    "qlin_tile_h_fp8.hip",
+    "qlin_tile_h_int8.hip",
     "qlin_tile_int8.hip",
     "qlin_tile_block.hip",
     "qlin_stream_lds_fp8.hip",
@@ -87,6 +91,14 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # host-side dispatch measurement program, linked against the library
+    tmp = DISPATCH_BENCH + ".tmp"
+    cmd = [hipcc()] + flags() + [os.path.join(PKG, "dispatch_bench.hip"), "-o", tmp, "-L", PKG,
+                                 "-lqlinear", "-Wl,-rpath,$ORIGIN"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"dispatch bench build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, DISPATCH_BENCH)
     if verbose:
         print(f"built {LIB}")
     return LIB

@@ -73,6 +73,8 @@ const Instance *tile_instances_int8(int *count);
 const Instance *tile_instances_block(int *count);
 const Instance *stream_lds_instances_fp8(int *count);
 const Instance *stream_lds_instances_int8(int *count);
+const Instance *tile_h_instances_fp8(int *count);
+const Instance *tile_h_instances_int8(int *count);
 
 // Split-K two-pass reduction + epilogue.
 hipError_t launch_reduce(int fmt, int scal, const KArgs &a, hipStream_t s);

@@ -79,6 +79,144 @@ __device__ inline v16f mma32_piece<FMT_E4M3>(const v4i *a, const v4i *b, int j, 
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 0, 0, 0);
 }
 
+// XCD-aware tile id -> origin (m0, n0) of the workgroup's output tile.
+// Consecutive workgroup ids land on different XCDs (round-robin over 8), so
+// ids are remapped to give every XCD a contiguous range of tiles, walked in
+// groups of GM token tiles so that the tiles an XCD runs together share A
+// rows and B rows in its own L2.
+template <int BM, int BN>
+__device__ inline void tile_origin(const KArgs &p, int &m0, int &n0)
+{
+    constexpr int GM = 4;
+    const int tiles_m = (p.M + BM - 1) / BM;
+    const int tiles_n = (p.N + BN - 1) / BN;
+    const int T = tiles_m * tiles_n;
+    int b = blockIdx.x;
+    const int per = T >> 3;
+    if (b < per * 8)
+        b = (b & 7) * per + (b >> 3);
+    const int group_tiles = GM * tiles_n;
+    const int grp = b / group_tiles;
+    const int first_m = grp * GM;
+    const int gsize = min(tiles_m - first_m, GM);
+    const int in_grp = b - grp * group_tiles;
+    m0 = (first_m + in_grp % gsize) * BM;
+    n0 = (in_grp / gsize) * BN;
+}
+
+// Epilogue of a tile: the wave's FM x FN accumulator blocks of 32x32 are
+// either scaled, rounded and stored (no split), or written as split-K
+// partials; with the last-arriver reduction the last workgroup of the tile
+// sums the partials in split order and stores the result.
+template <int FMT, int SCAL, bool SWAP, int BM, int BN, int WM, int WN>
+__device__ inline void tile_finish(const KArgs &p,
+                                   typename AccT<FMT>::v16 (&acc)[BM / WM / 32][BN / WN / 32],
+                                   int m0, int n0, int wm, int wn, int lane)
+{
+    typedef typename AccT<FMT>::v16 A16;
+    typedef typename AccT<FMT>::scalar AS;
+    constexpr int WTM = BM / WM;
+    constexpr int WTN = BN / WN;
+    constexpr int FM = WTM / 32;
+    constexpr int FN = WTN / 32;
+    const int fr = lane & 31;
+    const int fh = lane >> 5;
+    const int split = blockIdx.z;
+
+    // Output positions of acc[fm][fn][v] for this lane:
+    //   SWAP:     t = tok0 + fr,  n = wgt0 + 8*(v/4) + 4*fh + v%4  (4 consecutive n per v/4)
+    //   standard: t = tok0 + 8*(v/4) + 4*fh + v%4,  n = wgt0 + fr
+    // with tok0 = m0 + wm*WTM + 32*fm and wgt0 = n0 + wn*WTN + 32*fn.
+    auto emit = [&](const A16 (&val)[FM][FN]) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int tok0 = m0 + wm * WTM + 32 * fm;
+                const int wgt0 = n0 + wn * WTN + 32 * fn;
+                if (SWAP) {
+                    const int t = tok0 + fr;
+                    if (t >= p.M)
+                        continue;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int n = wgt0 + 8 * q + 4 * fh;
+                        typename AccT<FMT>::v4 v4v;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) v4v[j] = val[fm][fn][4 * q + j];
+                        if (n + 3 < p.N) {
+                            store_final4<FMT, SCAL>(p, t, n, v4v);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                if (n + j < p.N)
+                                    store_final<FMT, SCAL>(p, t, n + j, v4v[j]);
+                        }
+                    }
+                } else {
+                    const int n = wgt0 + fr;
+                    if (n >= p.N)
+                        continue;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int t = tok0 + 8 * (v >> 2) + 4 * fh + (v & 3);
+                        if (t < p.M)
+                            store_final<FMT, SCAL>(p, t, n, val[fm][fn][v]);
+                    }
+                }
+            }
+    };
+
+    if (p.split_k > 1) {
+        // Split-K partials (device-coherent stores for the last-arriver exchange)
+        const bool la = p.reduce == QLIN_REDUCE_LAST_ARRIVER;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int tok0 = m0 + wm * WTM + 32 * fm;
+                const int wgt0 = n0 + wn * WTN + 32 * fn;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int t = SWAP ? tok0 + fr : tok0 + 8 * (v >> 2) + 4 * fh + (v & 3);
+                    const int n = SWAP ? wgt0 + 8 * (v >> 2) + 4 * fh + (v & 3) : wgt0 + fr;
+                    if (t < p.M && n < p.N) {
+                        AS *d = part_ptr<FMT>(p, split, t, n);
+                        if (la)
+                            st_dev(d, (AS)acc[fm][fn][v]);
+                        else
+                            *d = acc[fm][fn][v];
+                    }
+                }
+            }
+        if (!la)
+            return;
+        if (!arrive_last(p.counters + blockIdx.x, p.split_k))
+            return;
+        // The last arriver sums every split's partial in split order (its
+        // own included), overwriting its accumulators.
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int tok0 = m0 + wm * WTM + 32 * fm;
+                const int wgt0 = n0 + wn * WTN + 32 * fn;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int t = SWAP ? tok0 + fr : tok0 + 8 * (v >> 2) + 4 * fh + (v & 3);
+                    const int n = SWAP ? wgt0 + 8 * (v >> 2) + 4 * fh + (v & 3) : wgt0 + fr;
+                    AS a = 0;
+                    if (t < p.M && n < p.N)
+                        for (int s = 0; s < p.split_k; ++s)
+                            a += ld_dev(part_ptr<FMT>(p, s, t, n));
+                    acc[fm][fn][v] = a;
+                }
+            }
+        rearm(p.counters + blockIdx.x);
+    }
+    emit(acc);
+}
+
 template <int FMT, int SCAL, bool SWAP, int BM, int BN, int WM, int WN, int S>
 __global__ void __launch_bounds__(64 * WM * WN)
 k_tile(KArgs p)
@@ -92,7 +230,6 @@ k_tile(KArgs p)
     constexpr int FN = WTN / 32;
     constexpr int ROWS = BM + BN;
     constexpr int STAGE = ROWS * 128;
-    constexpr int GM = 4;
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
     static_assert(ROWS % 8 == 0, "rows");
     static_assert(S >= 2 && S <= 4, "stages");
@@ -105,23 +242,8 @@ k_tile(KArgs p)
     const int wm = wave / WN;
     const int wn = wave % WN;
 
-    // ---- XCD-aware tile id -> (token tile, weight tile)
-    const int tiles_m = (p.M + BM - 1) / BM;
-    const int tiles_n = (p.N + BN - 1) / BN;
-    const int T = tiles_m * tiles_n;
-    int b = blockIdx.x;
-    const int per = T >> 3;
-    if (b < per * 8)
-        b = (b & 7) * per + (b >> 3);
-    const int group_tiles = GM * tiles_n;
-    const int grp = b / group_tiles;
-    const int first_m = grp * GM;
-    const int gsize = min(tiles_m - first_m, GM);
-    const int in_grp = b - grp * group_tiles;
-    const int tm = first_m + in_grp % gsize;
-    const int tn = in_grp / gsize;
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
+    int m0, n0;
+    tile_origin<BM, BN>(p, m0, n0);
 
     // ---- K range of this split (128-byte steps)
     const int KS = p.K >> 7;
@@ -287,102 +409,7 @@ k_tile(KArgs p)
         }
     }
 
-    // Output positions of acc[fm][fn][v] for this lane:
-    //   SWAP:     t = tok0 + fr,  n = wgt0 + 8*(v/4) + 4*fh + v%4  (4 consecutive n per v/4)
-    //   standard: t = tok0 + 8*(v/4) + 4*fh + v%4,  n = wgt0 + fr
-    // with tok0 = m0 + wm*WTM + 32*fm and wgt0 = n0 + wn*WTN + 32*fn.
-    auto emit = [&](const A16 (&val)[FM][FN]) {
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const int tok0 = m0 + wm * WTM + 32 * fm;
-                const int wgt0 = n0 + wn * WTN + 32 * fn;
-                if (SWAP) {
-                    const int t = tok0 + fr;
-                    if (t >= p.M)
-                        continue;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int n = wgt0 + 8 * q + 4 * fh;
-                        typename AccT<FMT>::v4 v4v;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) v4v[j] = val[fm][fn][4 * q + j];
-                        if (n + 3 < p.N) {
-                            store_final4<FMT, SCAL>(p, t, n, v4v);
-                        } else {
-#pragma unroll
-                            for (int j = 0; j < 4; ++j)
-                                if (n + j < p.N)
-                                    store_final<FMT, SCAL>(p, t, n + j, v4v[j]);
-                        }
-                    }
-                } else {
-                    const int n = wgt0 + fr;
-                    if (n >= p.N)
-                        continue;
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int t = tok0 + 8 * (v >> 2) + 4 * fh + (v & 3);
-                        if (t < p.M)
-                            store_final<FMT, SCAL>(p, t, n, val[fm][fn][v]);
-                    }
-                }
-            }
-    };
-
-    if (p.split_k == 1) {
-        emit(acc);
-        return;
-    }
-
-    // Split-K partials (device-coherent stores for the last-arriver exchange)
-    const bool la = p.reduce == QLIN_REDUCE_LAST_ARRIVER;
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int tok0 = m0 + wm * WTM + 32 * fm;
-            const int wgt0 = n0 + wn * WTN + 32 * fn;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int t = SWAP ? tok0 + fr : tok0 + 8 * (v >> 2) + 4 * fh + (v & 3);
-                const int n = SWAP ? wgt0 + 8 * (v >> 2) + 4 * fh + (v & 3) : wgt0 + fr;
-                if (t < p.M && n < p.N) {
-                    AS *d = part_ptr<FMT>(p, split, t, n);
-                    if (la)
-                        st_dev(d, (AS)acc[fm][fn][v]);
-                    else
-                        *d = acc[fm][fn][v];
-                }
-            }
-        }
-    if (!la)
-        return;
-
-    const int tile = blockIdx.x;
-    if (!arrive_last(p.counters + tile, p.split_k))
-        return;
-    A16 sum[FM][FN];
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int tok0 = m0 + wm * WTM + 32 * fm;
-            const int wgt0 = n0 + wn * WTN + 32 * fn;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int t = SWAP ? tok0 + fr : tok0 + 8 * (v >> 2) + 4 * fh + (v & 3);
-                const int n = SWAP ? wgt0 + 8 * (v >> 2) + 4 * fh + (v & 3) : wgt0 + fr;
-                AS a = 0;
-                if (t < p.M && n < p.N)
-                    for (int s = 0; s < p.split_k; ++s)
-                        a += ld_dev(part_ptr<FMT>(p, s, t, n));
-                sum[fm][fn][v] = a;
-            }
-        }
-    emit(sum);
-    rearm(p.counters + tile);
+    tile_finish<FMT, SCAL, SWAP, BM, BN, WM, WN>(p, acc, m0, n0, wm, wn, lane);
 }
 
 template <int FMT, int SCAL, bool SWAP, int BM, int BN, int WM, int WN, int S>

@@ -46,7 +46,7 @@ def candidates(fmt: str, M: int, N: int, K: int, max_split: int = 256):
     for base in q.instances_for(fmt):
         if base.kernel in (q.KERNEL_STREAM, q.KERNEL_STREAM_LDS) and -(-M // base.tile_m) > 4:
             continue                      # the stream kernels are for small token counts
-        if base.kernel == q.KERNEL_TILE and M < 32:
+        if base.kernel == q.KERNEL_TILE and M < 16:
             continue
         split = 1
         while split <= min(max_split, 256):

@@ -192,3 +192,32 @@ def test_compiled_in_table_entries_are_valid():
         assert q.select_config(fmt, M, N, K) == c, ln
         n += 1
     assert n == q.config_table_size()
+
+
+def qtok(dt=q.E4M3, M=4, K=1024, X=A16, ldx=None, Q=B16, ldq=None, S=S4):
+    return q.lib().qlin_quant_per_token(dt, M, K, X, K if ldx is None else ldx, Q,
+                                        K if ldq is None else ldq, S, None)
+
+
+def qgrp(M=4, K=1024, X=A16, ldx=None, Q=B16, ldq=None, S=S4):
+    return q.lib().qlin_quant_per_group128(M, K, X, K if ldx is None else ldx, Q,
+                                           K if ldq is None else ldq, S, None)
+
+
+def test_quant_validation_errors():
+    assert qtok(dt=5) == ST["arg"]
+    assert qtok(M=-1) == ST["shape"]
+    assert qtok(K=0) == ST["shape"]
+    assert qtok(K=24) == ST["shape"]
+    assert qgrp(K=1040) == ST["shape"]                  # groups need K % 128
+    assert qtok(M=0, X=None, Q=None, S=None) == ST["ok"]
+    assert qgrp(M=0, X=None, Q=None, S=None) == ST["ok"]
+    assert qtok(X=None) == ST["null"]
+    assert qtok(S=None) == ST["null"]
+    assert qgrp(Q=None) == ST["null"]
+    assert qtok(ldx=1000) == ST["stride"]               # ldx < K
+    assert qtok(ldx=1028) == ST["stride"]               # ldx % 8
+    assert qtok(ldq=1032) == ST["stride"]               # ldq % 16
+    assert qtok(X=A16 + 8) == ST["align"]
+    assert qgrp(Q=B16 + 4) == ST["align"]
+    assert qtok(S=S4 + 2) == ST["align"]
