@@ -44,6 +44,8 @@ WORKLOAD_TEXT = {
     "all_32b": "FP8_Dynamic, W8A8_INT8 and Block_FP8 on 32B-class linears (K,N) in "
                "{(5120,10240),(8192,5120),(5120,51200),(25600,5120)} x M in {1,2,4,8,16,24,32,2048}",
     "fp8_small": "FP8_Dynamic scaled_mm, M=16 N=512 K=1024",
+    "prefill": "the M >= 512 points: FP8_Dynamic and Block_FP8 8B-class at M=512, all three "
+               "formats on the 32B-class linears at M=2048",
 }
 
 
@@ -195,6 +197,43 @@ def cpu_baseline(wl: Workload, threads: int, budget_s: float):
     return done_bytes, done_flops, secs, n_calls, first
 
 
+def prefill_points(reps: int = 4):
+    """Per-point GEMM time of the MFMA-bound (M >= 512) points: a graph of
+    `reps` launches per point on alternating weight copies, replayed twice,
+    timed with events on the launch stream."""
+    import torch
+    wl = Workload("prefill", copies_target_bytes=0)
+    wl.call(wl.items[0], 0)
+    torch.cuda.synchronize()
+    out = []
+    for it in wl.items:
+        g = capture(lambda it=it: [wl.call(it, r % wl.sets) for r in range(reps)])
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (2 * reps)
+        del g
+        tf = it["flops"] / us / 1e6
+        c = it["cfg"]
+        out.append({"fmt": it["fmt"], "M": it["M"], "N": it["N"], "K": it["K"], "us": round(us, 2),
+                    "tflops": round(tf, 1), "frac": round(tf / MFMA_PEAK_TOPS, 4),
+                    "cfg": f"k{c.kernel} v{c.variant} {c.tile_m}x{c.tile_n}x{c.tile_k} "
+                           f"w{c.waves_n}x{c.waves_k} s{c.stages} split{c.split_k}"})
+    del wl
+    torch.cuda.empty_cache()
+    tfs = np.array([p["tflops"] for p in out])
+    geo = float(np.exp(np.log(tfs).mean()))
+    return {"unit": "TFLOP/s", "peak": MFMA_PEAK_TOPS, "geomean_tflops": round(geo, 1),
+            "geomean_frac": round(geo / MFMA_PEAK_TOPS, 4), "min_frac": round(float(tfs.min()) / MFMA_PEAK_TOPS, 4),
+            "max_frac": round(float(tfs.max()) / MFMA_PEAK_TOPS, 4), "points": out}
+
+
 def cpu_model() -> str:
     try:
         for ln in open("/proc/cpuinfo"):
@@ -247,6 +286,7 @@ def main():
     ap.add_argument("--table", default=None, help="config table file to load before running")
     ap.add_argument("--per-point", action="store_true", help="print per-point timings to stderr")
     ap.add_argument("--no-dispatch", action="store_true", help="skip the host dispatch-cost run")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the M >= 512 per-point timings")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -317,6 +357,9 @@ def main():
                "host_cpu": cpu_model()}
 
     dispatch = None if args.no_dispatch else dispatch_cost()
+    prefill = None
+    if not args.no_prefill and args.workload != "prefill":
+        prefill = prefill_points()
 
     flops_tops = wl.flops_per_step / (ms_step * 1e-3) / 1e12
     out = {
@@ -348,6 +391,7 @@ def main():
                      "traffic_src": traffic_src},
         "cpu_baseline": cpu,
         "dispatch": dispatch,
+        "prefill_mfma": prefill,
         "parity_vs_oracle": parity_ok,
     }
     print(json.dumps(out), flush=True)

@@ -230,17 +230,24 @@ __device__ inline T ld_dev(T *p)
 
 // Every thread of the workgroup calls this after writing its partials with
 // st_dev.  Returns true (in all threads) for the workgroup whose increment
-// brought the tile's counter to split_k.
-__device__ inline bool arrive_last(int32_t *counter, int split_k)
+// brought the tile's counter to split_k.  `flag` is one int of LDS for the
+// broadcast; the caller may pass memory of a pipeline ring it no longer reads
+// (the barrier below orders it after every wave's last use).
+__device__ inline bool arrive_last(int32_t *counter, int split_k, int *flag)
 {
-    __shared__ int s_last;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // own partial stores acknowledged
     __syncthreads();
     if (threadIdx.x == 0)
-        s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                 split_k - 1;
+        *flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                split_k - 1;
     __syncthreads();
-    return s_last != 0;
+    return *flag != 0;
+}
+
+__device__ inline bool arrive_last(int32_t *counter, int split_k)
+{
+    __shared__ int s_last;
+    return arrive_last(counter, split_k, &s_last);
 }
 
 // The last arriver re-arms the counter for the next call (stream order makes

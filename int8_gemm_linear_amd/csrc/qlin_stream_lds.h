@@ -8,7 +8,10 @@
 // The LDS round trip costs nothing that matters here: LDS bandwidth is far
 // above a CU's share of HBM bandwidth.
 //
-// Workgroup: NW waves own TR = 16*RB weight rows and TMS tokens (1..32; the
+// Workgroup: NW waves own TR = 8, 16 or 32 weight rows (the matrix core sees
+// blocks of 16; with 8 rows, fragment rows 8..15 repeat rows 0..7 and their
+// outputs are dropped, which doubles the workgroup count for small N without
+// a split-K reduction) and TMS tokens (1..32; the
 // matrix core sees them as TB = ceil(TMS/16) blocks of 16, the rows past TMS
 // hold stale data that only feeds outputs never stored) of one K split.  The
 // split's K range is cut into chunks of CHK bytes; a chunk stage in LDS holds
@@ -52,14 +55,17 @@ __device__ inline void wait_vm()
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int FMT, bool SWAP, int TMS, int RB, int NW, int S, int CHK>
+template <int FMT, bool SWAP, int TMS, int TRW, int NW, int S, int CHK>
 __global__ void __launch_bounds__(64 * NW)
 k_stream_lds(KArgs p)
 {
     typedef typename AccT<FMT>::v4 A4;
     typedef typename AccT<FMT>::scalar AS;
     constexpr int TB = (TMS + 15) / 16;
-    constexpr int TR = 16 * RB;
+    constexpr int TR = TRW;                          // weight rows of the workgroup
+    constexpr int RB = TR >= 16 ? TR / 16 : 1;       // 16-row matrix-core blocks
+    constexpr int RMASK = TR >= 16 ? 15 : TR - 1;    // fragment row within the stage
+    static_assert(TR == 8 || TR == 16 || TR == 32, "weight rows");
     constexpr int RPI = 1024 / CHK;                  // rows per load instruction
     constexpr int ROWS0 = TR + TMS;
     constexpr int INSTR = ((ROWS0 + RPI * NW - 1) / (RPI * NW)) * NW;   // padded
@@ -192,9 +198,11 @@ k_stream_lds(KArgs p)
             for (int h = 0; h < 2; ++h) {
                 const int piece = s * 8 + h * 4 + g;
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    bf[rb][h] = *reinterpret_cast<const v4i *>(st + (rb * 16 + r16) * CHK +
-                                                                16 * (piece ^ r16));
+                for (int rb = 0; rb < RB; ++rb) {
+                    const int wr = rb * 16 + (r16 & RMASK);
+                    bf[rb][h] = *reinterpret_cast<const v4i *>(st + wr * CHK +
+                                                                16 * (piece ^ (wr & 15)));
+                }
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb)
                     af[tb][h] = *reinterpret_cast<const v4i *>(st + arow[tb] * CHK +
@@ -244,6 +252,7 @@ k_stream_lds(KArgs p)
     //   SWAP:     n = n0 + 16*rb + 4*g + v,  t = m0 + 16*tb + r16
     //   standard: n = n0 + 16*rb + r16,      t = m0 + 16*tb + 4*g + v
     const int mend = min(p.M, m0 + TMS);           // tokens of this tile
+    const int nend = min(p.N, n0 + TR);            // weight rows of this tile
     auto emit = [&](const A4 (&val)[RB][TB]) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -252,29 +261,29 @@ k_stream_lds(KArgs p)
                 if (SWAP) {
                     const int t = m0 + tb * 16 + r16;
                     const int n = n0 + rb * 16 + 4 * g;
-                    if (t >= mend)
+                    if (t >= mend || n >= nend)
                         continue;
                     if (!scaled) {
-                        if (n + 3 < p.N) {
+                        if (n + 3 < nend) {
                             store_final4<FMT, SC_TC>(p, t, n, val[rb][tb]);
                         } else {
 #pragma unroll
                             for (int v = 0; v < 4; ++v)
-                                if (n + v < p.N)
+                                if (n + v < nend)
                                     store_final<FMT, SC_TC>(p, t, n + v, val[rb][tb][v]);
                         }
-                    } else if (n + 3 < p.N) {
+                    } else if (n + 3 < nend) {
                         store_final4_pre<FMT, SC_TC>(p, t, n, val[rb][tb], sa1[tb], sb4[rb]);
                     } else {
 #pragma unroll
                         for (int v = 0; v < 4; ++v)
-                            if (n + v < p.N)
+                            if (n + v < nend)
                                 p.Y[(int64_t)t * p.ldy + n + v] =
                                     bf16_bits(((float)val[rb][tb][v] * sa1[tb]) * sb4[rb][v]);
                     }
                 } else {
                     const int n = n0 + rb * 16 + r16;
-                    if (n >= p.N)
+                    if (n >= nend)
                         continue;
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
@@ -307,7 +316,7 @@ k_stream_lds(KArgs p)
                 for (int v = 0; v < 4; ++v) {
                     const int t = SWAP ? m0 + tb * 16 + r16 : m0 + tb * 16 + 4 * g + v;
                     const int n = SWAP ? n0 + rb * 16 + 4 * g + v : n0 + rb * 16 + r16;
-                    if (t < mend && n < p.N) {
+                    if (t < mend && n < nend) {
                         AS *d = part_ptr<FMT>(p, split, t, n);
                         if (la)
                             st_dev(d, (AS)acc[rb][tb][v]);
@@ -333,7 +342,7 @@ k_stream_lds(KArgs p)
                     for (int v = 0; v < 4; ++v) {
                         const int t = SWAP ? m0 + tb * 16 + r16 : m0 + tb * 16 + 4 * g + v;
                         const int n = SWAP ? n0 + rb * 16 + 4 * g + v : n0 + rb * 16 + r16;
-                        if (t < mend && n < p.N)
+                        if (t < mend && n < nend)
                             sum[rb][tb][v] += ld_dev(part_ptr<FMT>(p, s, t, n));
                     }
             }
@@ -342,24 +351,28 @@ k_stream_lds(KArgs p)
     rearm(p.counters + tile);
 }
 
-template <int FMT, bool SWAP, int TMS, int RB, int NW, int S, int CHK>
+template <int FMT, bool SWAP, int TMS, int TRW, int NW, int S, int CHK>
 hipError_t launch_stream_lds(const KArgs &a, dim3 grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_stream_lds<FMT, SWAP, TMS, RB, NW, S, CHK>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((k_stream_lds<FMT, SWAP, TMS, TRW, NW, S, CHK>), grid, dim3(64 * NW), 0, s, a);
     return hipGetLastError();
 }
 
-#define QLIN_STREAM_LDS_INSTANCE(FMT, BIT, SW, TMS, RB, NW, S, CHK)                      \
-    {{QLIN_KERNEL_STREAM_LDS, SW, TMS, 16 * (RB), CHK, 1, NW, S, 1, 0}, BIT, FMT, SC_TC, \
-     &launch_stream_lds<FMT, (SW) != 0, TMS, RB, NW, S, CHK>}
+#define QLIN_STREAM_LDS_INSTANCE(FMT, BIT, SW, TMS, TRW, NW, S, CHK)                 \
+    {{QLIN_KERNEL_STREAM_LDS, SW, TMS, TRW, CHK, 1, NW, S, 1, 0}, BIT, FMT, SC_TC, \
+     &launch_stream_lds<FMT, (SW) != 0, TMS, TRW, NW, S, CHK>}
 
-// (RB, NW, S, CHK) per token count TMS; LDS per workgroup is about
-// S * (16*RB + TMS) * CHK bytes.
+// (weight rows, NW, S, CHK) per token count TMS; LDS per workgroup is about
+// S * (rows + TMS) * CHK bytes.  8-row tiles double the workgroup count for
+// small N (the matrix core still sees 16 rows; rows 8..15 repeat 0..7 and
+// their outputs are not stored).
 #define QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, TMS) \
-    X(FMT, BIT, SW, TMS, 1, 4, 2, 1024),            \
-    X(FMT, BIT, SW, TMS, 1, 8, 2, 1024),            \
-    X(FMT, BIT, SW, TMS, 1, 4, 4, 512),             \
-    X(FMT, BIT, SW, TMS, 1, 8, 3, 1024)
+    X(FMT, BIT, SW, TMS, 16, 4, 2, 1024),           \
+    X(FMT, BIT, SW, TMS, 16, 8, 2, 1024),           \
+    X(FMT, BIT, SW, TMS, 16, 4, 4, 512),            \
+    X(FMT, BIT, SW, TMS, 16, 8, 3, 1024),           \
+    X(FMT, BIT, SW, TMS, 8, 8, 2, 1024),            \
+    X(FMT, BIT, SW, TMS, 8, 4, 2, 1024)
 
 #define QLIN_STREAM_LDS_SHAPES(X, FMT, BIT, SW)    \
     QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 1),      \
@@ -368,7 +381,7 @@ hipError_t launch_stream_lds(const KArgs &a, dim3 grid, hipStream_t s)
     QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 8),      \
     QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 16),     \
     QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 32),     \
-    X(FMT, BIT, SW, 16, 2, 4, 2, 1024),            \
-    X(FMT, BIT, SW, 32, 2, 8, 2, 1024)
+    X(FMT, BIT, SW, 16, 32, 4, 2, 1024),           \
+    X(FMT, BIT, SW, 32, 32, 8, 2, 1024)
 
 }  // namespace qlin

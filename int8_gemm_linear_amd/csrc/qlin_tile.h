@@ -111,7 +111,7 @@ __device__ inline void tile_origin(const KArgs &p, int &m0, int &n0)
 template <int FMT, int SCAL, bool SWAP, int BM, int BN, int WM, int WN>
 __device__ inline void tile_finish(const KArgs &p,
                                    typename AccT<FMT>::v16 (&acc)[BM / WM / 32][BN / WN / 32],
-                                   int m0, int n0, int wm, int wn, int lane)
+                                   int m0, int n0, int wm, int wn, int lane, uint8_t *lds)
 {
     typedef typename AccT<FMT>::v16 A16;
     typedef typename AccT<FMT>::scalar AS;
@@ -127,15 +127,33 @@ __device__ inline void tile_finish(const KArgs &p,
     //   SWAP:     t = tok0 + fr,  n = wgt0 + 8*(v/4) + 4*fh + v%4  (4 consecutive n per v/4)
     //   standard: t = tok0 + 8*(v/4) + 4*fh + v%4,  n = wgt0 + fr
     // with tok0 = m0 + wm*WTM + 32*fm and wgt0 = n0 + wn*WTN + 32*fn.
+    //
+    // The scales are gathered into registers before any output store: the
+    // compiler must assume Y may alias sA/sB, so loads interleaved with the
+    // stores would each wait a full memory latency.
+    const bool scaled = SCAL == SC_TC && !(FMT == FMT_INT8 && p.acc_out);
     auto emit = [&](const A16 (&val)[FM][FN]) {
+        if (SWAP) {
+            float sa_r[FM];
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
+            for (int fm = 0; fm < FM; ++fm) {
+                const int t = m0 + wm * WTM + 32 * fm + fr;
+                sa_r[fm] = scaled && t < p.M ? p.sA[t] : 0.f;
+            }
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                const int tok0 = m0 + wm * WTM + 32 * fm;
                 const int wgt0 = n0 + wn * WTN + 32 * fn;
-                if (SWAP) {
-                    const int t = tok0 + fr;
+                v4f sb_r[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = wgt0 + 8 * q + 4 * fh;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        sb_r[q][j] = scaled && n + j < p.N ? p.sB[n + j] : 0.f;
+                }
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    const int t = m0 + wm * WTM + 32 * fm + fr;
                     if (t >= p.M)
                         continue;
 #pragma unroll
@@ -144,7 +162,9 @@ __device__ inline void tile_finish(const KArgs &p,
                         typename AccT<FMT>::v4 v4v;
 #pragma unroll
                         for (int j = 0; j < 4; ++j) v4v[j] = val[fm][fn][4 * q + j];
-                        if (n + 3 < p.N) {
+                        if (scaled && n + 3 < p.N) {
+                            store_final4_pre<FMT, SCAL>(p, t, n, v4v, sa_r[fm], sb_r[q]);
+                        } else if (n + 3 < p.N) {
                             store_final4<FMT, SCAL>(p, t, n, v4v);
                         } else {
 #pragma unroll
@@ -153,18 +173,138 @@ __device__ inline void tile_finish(const KArgs &p,
                                     store_final<FMT, SCAL>(p, t, n + j, v4v[j]);
                         }
                     }
-                } else {
-                    const int n = wgt0 + fr;
-                    if (n >= p.N)
-                        continue;
+                }
+            }
+        } else {
+            v4f sa_r[FM][4];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int t = m0 + wm * WTM + 32 * fm + 8 * q + 4 * fh + j;
+                        sa_r[fm][q][j] = scaled && t < p.M ? p.sA[t] : 0.f;
+                    }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int n = n0 + wn * WTN + 32 * fn + fr;
+                if (n >= p.N)
+                    continue;
+                const float sb = scaled ? p.sB[n] : 0.f;
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    const int tok0 = m0 + wm * WTM + 32 * fm;
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int t = tok0 + 8 * (v >> 2) + 4 * fh + (v & 3);
-                        if (t < p.M)
+                        if (t >= p.M)
+                            continue;
+                        if (scaled)
+                            p.Y[(int64_t)t * p.ldy + n] =
+                                bf16_bits(((float)val[fm][fn][v] * sa_r[fm][v >> 2][v & 3]) * sb);
+                        else
                             store_final<FMT, SCAL>(p, t, n, val[fm][fn][v]);
                     }
                 }
             }
+        }
+    };
+
+    // Staged bf16 store: the workgroup's BM x BN output tile is assembled in
+    // LDS (the pipeline ring, free once every wave has left the main loop)
+    // and written back as whole 16-byte pieces of contiguous rows, so every
+    // store instruction covers full 128-byte lines of Y instead of 32 rows x
+    // 16 bytes.  Row stride BN*2 bytes; the CPR 16-byte chunks of a row are
+    // XOR-swizzled by the row index against LDS bank conflicts.
+    constexpr int CPR = BN / 8;                       // 16-byte chunks per row
+    static_assert((CPR & (CPR - 1)) == 0, "chunks per row");
+    constexpr int NT = 64 * WM * WN;
+    auto stage_off = [&](int r, int c) { return r * (BN * 2) + 16 * (c ^ (r & (CPR - 1))); };
+    auto emit_staged = [&](const A16 (&val)[FM][FN]) {
+        __syncthreads();                               // every wave is done with the ring
+        if (SWAP) {
+            float sa_r[FM];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int t = m0 + wm * WTM + 32 * fm + fr;
+                sa_r[fm] = scaled && t < p.M ? p.sA[t] : 1.f;
+            }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int nl0 = wn * WTN + 32 * fn;           // tile-local column of the block
+                v4f sb_r[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int n = n0 + nl0 + 8 * q + 4 * fh + j;
+                        sb_r[q][j] = scaled && n < p.N ? p.sB[n] : 1.f;
+                    }
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    const int r = wm * WTM + 32 * fm + fr;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        uint16_t h[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float x = (float)val[fm][fn][4 * q + j];
+                            h[j] = bf16_bits(scaled ? (x * sa_r[fm]) * sb_r[q][j] : x);
+                        }
+                        uint2 w;
+                        w.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+                        w.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+                        *reinterpret_cast<uint2 *>(lds + stage_off(r, (nl0 >> 3) + q) + 8 * fh) = w;
+                    }
+                }
+            }
+        } else {
+            v4f sa_r[FM][4];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int t = m0 + wm * WTM + 32 * fm + 8 * q + 4 * fh + j;
+                        sa_r[fm][q][j] = scaled && t < p.M ? p.sA[t] : 1.f;
+                    }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int nl = wn * WTN + 32 * fn + fr;
+                const float sb = scaled && n0 + nl < p.N ? p.sB[n0 + nl] : 1.f;
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int r = wm * WTM + 32 * fm + 8 * (v >> 2) + 4 * fh + (v & 3);
+                        const float x = (float)val[fm][fn][v];
+                        *reinterpret_cast<uint16_t *>(lds + stage_off(r, nl >> 3) + 2 * (nl & 7)) =
+                            bf16_bits(scaled ? (x * sa_r[fm][v >> 2][v & 3]) * sb : x);
+                    }
+            }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int k = threadIdx.x; k < BM * CPR; k += NT) {
+            const int r = k / CPR;
+            const int c = k % CPR;
+            const int t = m0 + r;
+            const int n = n0 + 8 * c;
+            if (t >= p.M || n >= p.N)
+                continue;
+            const v4i d = *reinterpret_cast<const v4i *>(lds + stage_off(r, c));
+            uint16_t *y = p.Y + (int64_t)t * p.ldy + n;
+            if (n + 8 <= p.N) {
+                *reinterpret_cast<v4i *>(y) = d;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (n + j < p.N)
+                        y[j] = (uint16_t)((uint32_t)d[j >> 1] >> (16 * (j & 1)));
+            }
+        }
     };
 
     if (p.split_k > 1) {
@@ -191,7 +331,7 @@ __device__ inline void tile_finish(const KArgs &p,
             }
         if (!la)
             return;
-        if (!arrive_last(p.counters + blockIdx.x, p.split_k))
+        if (!arrive_last(p.counters + blockIdx.x, p.split_k, reinterpret_cast<int *>(lds)))
             return;
         // The last arriver sums every split's partial in split order (its
         // own included), overwriting its accumulators.
@@ -213,6 +353,12 @@ __device__ inline void tile_finish(const KArgs &p,
                 }
             }
         rearm(p.counters + blockIdx.x);
+    }
+    if (scaled || SCAL == SC_BLOCK) {
+        if ((p.ldy & 7) == 0) {
+            emit_staged(acc);
+            return;
+        }
     }
     emit(acc);
 }
@@ -409,7 +555,8 @@ k_tile(KArgs p)
         }
     }
 
-    tile_finish<FMT, SCAL, SWAP, BM, BN, WM, WN>(p, acc, m0, n0, wm, wn, lane);
+    static_assert(BM * BN * 2 <= S * STAGE, "the output tile is staged in the ring");
+    tile_finish<FMT, SCAL, SWAP, BM, BN, WM, WN>(p, acc, m0, n0, wm, wn, lane, lds);
 }
 
 template <int FMT, int SCAL, bool SWAP, int BM, int BN, int WM, int WN, int S>
@@ -431,6 +578,7 @@ hipError_t launch_tile(const KArgs &a, dim3 grid, hipStream_t s)
     X(FMT, SCAL, BIT, SW, 128, 128, 2, 2, 4),   \
     X(FMT, SCAL, BIT, SW, 128, 256, 2, 2, 3),   \
     X(FMT, SCAL, BIT, SW, 256, 128, 2, 2, 3),   \
+    X(FMT, SCAL, BIT, SW, 256, 256, 2, 2, 2),   \
     X(FMT, SCAL, BIT, SW, 256, 256, 2, 4, 2),   \
     X(FMT, SCAL, BIT, SW, 256, 256, 4, 2, 2),   \
     X(FMT, SCAL, BIT, SW, 256, 128, 4, 2, 3),   \

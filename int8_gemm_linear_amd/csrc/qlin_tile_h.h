@@ -23,9 +23,11 @@
 // a half-step is the only point where the waves meet.
 //
 // LDS stage: [BM rows of A][BN rows of B], 64 bytes per row.  The four
-// 16-byte chunks of stage row r are stored at slot c ^ swz64(r), which
-// keeps the rows a ds_read_b128 serves together on distinct banks whether
-// the LDS serves 128 or 256 bytes per clock.  global_load_lds writes lane
+// 16-byte chunks of stage row r are stored at slot c ^ swz64(r).  The
+// swizzle was chosen by measurement: for this read pattern (lane l reads
+// row l % 32, chunk pair l / 32) it sustains ~240 bytes per clock per CU of
+// ds_read_b128, where the unswizzled layout gets a quarter of that and
+// swizzles keyed on r >> 1 half.  global_load_lds writes lane
 // i's 16 bytes to slot (i % 4) of row (i / 4) of its 1 KB, so the swizzle
 // is applied on the global side: lane i fetches chunk (i % 4) ^ swz64(row).
 //
@@ -40,7 +42,7 @@
 
 namespace qlin {
 
-__device__ inline int swz64(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ inline int swz64(int r) { return ((r >> 2) ^ (r >> 3)) & 3; }
 
 // s_waitcnt vmcnt(L * n) lgkmcnt(0) for a run-time n in [0, NMAX].
 template <int L, int NMAX>
@@ -114,6 +116,7 @@ k_tile_h(KArgs p)
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
     static_assert(BM % 32 == 0 && GROUPS % NW == 0, "copies must split evenly over the waves");
     static_assert(S >= 3 && S <= 8, "stages");
+    static_assert(S * STAGE <= 160 * 1024, "LDS");
     static_assert(L * (S - 1) <= 63, "vmcnt range");
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[S * STAGE];
@@ -160,7 +163,8 @@ k_tile_h(KArgs p)
     };
 
     // Fragment addresses inside a stage: row r = base row + fr, chunks
-    // 2*fh and 2*fh + 1 (swz64 depends only on r mod 32, i.e. on fr).
+    // 2*fh and 2*fh + 1 (base rows are multiples of 32 and swz64(r + 32) =
+    // swz64(r), so the swizzle depends on fr only).
     const int sw = swz64(fr);
     const int off0 = fr * 64 + 16 * ((2 * fh) ^ sw);
     const int off1 = fr * 64 + 16 * ((2 * fh + 1) ^ sw);
@@ -242,7 +246,8 @@ k_tile_h(KArgs p)
         }
     }
 
-    tile_finish<FMT, SC_TC, SWAP, BM, BN, WM, WN>(p, acc, m0, n0, wm, wn, lane);
+    static_assert(BM * BN * 2 <= S * STAGE, "the output tile is staged in the ring");
+    tile_finish<FMT, SC_TC, SWAP, BM, BN, WM, WN>(p, acc, m0, n0, wm, wn, lane, lds);
 }
 
 template <int FMT, bool SWAP, int BM, int BN, int WM, int WN, int S>
@@ -259,6 +264,11 @@ hipError_t launch_tile_h(const KArgs &a, dim3 grid, hipStream_t s)
 
 // (BM, BN, WM, WN, S); LDS = S * (BM + BN) * 64 B.
 #define QLIN_TILE_H_SHAPES(X, FMT, BIT, SW) \
+    X(FMT, BIT, SW, 256, 256, 2, 4, 5),     \
+    X(FMT, BIT, SW, 256, 256, 4, 2, 5),     \
+    X(FMT, BIT, SW, 256, 256, 2, 4, 4),     \
+    X(FMT, BIT, SW, 256, 256, 4, 2, 4),     \
+    X(FMT, BIT, SW, 256, 128, 4, 2, 6),     \
     X(FMT, BIT, SW, 256, 256, 2, 2, 4),     \
     X(FMT, BIT, SW, 256, 128, 2, 2, 6),     \
     X(FMT, BIT, SW, 128, 256, 2, 2, 6),     \

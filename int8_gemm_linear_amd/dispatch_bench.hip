@@ -8,9 +8,13 @@
 // libqlinear.so, from C:
 //   select_us   qlin_select_config (table lookup) per call
 //   reject_us   a call that fails validation (argument checks only)
-//   launch_us   host time per qlin_scaled_mm call that launches (bursts of
-//               BURST calls, the queue never fills), median over bursts
-//   empty_launch_us  host time per launch of an empty kernel (HIP's floor)
+//   launch_us   host time per qlin_scaled_mm call that launches, enqueued
+//               in bursts of BURST calls behind a ~2 ms busy kernel (so the
+//               GPU consumes nothing while the host enqueues), median over
+//               bursts
+//   empty_launch_us  the same for an empty kernel (HIP's own floor)
+//   args_launch_us   the same for an empty kernel with a GEMM-sized argument
+//                    block and a GEMM-sized grid
 //   graph_launch_us  host time of one hipGraphLaunch of a graph of BURST calls
 //   graph_gpu_us_per_call  GPU time per call inside the replayed graph
 // Prints one JSON line.  Usage: qlin_dispatch_bench [M N K]  (W8A8_INT8).
@@ -35,6 +39,25 @@
     } while (0)
 
 __global__ void k_empty() {}
+
+// An empty kernel taking an argument block the size of the GEMM kernels'.
+struct ArgBlock {
+    void *p[8];
+    int v[14];
+};
+__global__ void k_args(ArgBlock a)
+{
+    if (a.v[0] == 12345)
+        static_cast<int *>(a.p[0])[0] = a.v[1];
+}
+
+// Keeps the GPU busy for about `cycles` shader clocks (bounded loop).
+__global__ void k_busy(long long cycles)
+{
+    const long long t0 = clock64();
+    while (clock64() - t0 < cycles) {
+    }
+}
 
 static double now_us()
 {
@@ -94,9 +117,12 @@ int main(int argc, char **argv)
         qlin_scaled_mm(QLIN_INT8, M, N, 24, A, K, sA, B, K, sB, Y, N, ws, wsb, s);   // K % 16 != 0
     const double reject_us = (now_us() - t0) / NQ;
 
-    // launching calls, bursts that fit the queue
+    // launching calls: enqueue a burst while the GPU is held by a busy
+    // kernel, so the host time is the enqueue cost alone
+    const long long busy = 5000000;                       // ~2 ms of shader clocks
     std::vector<double> per;
     for (int r = 0; r < REPS; ++r) {
+        hipLaunchKernelGGL(k_busy, dim3(1), dim3(64), 0, s, busy);
         t0 = now_us();
         for (int i = 0; i < BURST; ++i)
             call();
@@ -106,6 +132,7 @@ int main(int argc, char **argv)
     const double launch_us = median(per);
     per.clear();
     for (int r = 0; r < REPS; ++r) {
+        hipLaunchKernelGGL(k_busy, dim3(1), dim3(64), 0, s, busy);
         t0 = now_us();
         for (int i = 0; i < BURST; ++i)
             hipLaunchKernelGGL(k_empty, dim3(1), dim3(64), 0, s);
@@ -113,6 +140,17 @@ int main(int argc, char **argv)
         CK(hipStreamSynchronize(s));
     }
     const double empty_us = median(per);
+    per.clear();
+    ArgBlock ab{};
+    for (int r = 0; r < REPS; ++r) {
+        hipLaunchKernelGGL(k_busy, dim3(1), dim3(64), 0, s, busy);
+        t0 = now_us();
+        for (int i = 0; i < BURST; ++i)
+            hipLaunchKernelGGL(k_args, dim3(128), dim3(512), 0, s, ab);
+        per.push_back((now_us() - t0) / BURST);
+        CK(hipStreamSynchronize(s));
+    }
+    const double args_us = median(per);
 
     // graph of BURST calls: host cost of one replay, GPU time per call
     hipGraph_t g;
@@ -141,10 +179,11 @@ int main(int argc, char **argv)
     }
     std::printf("{\"shape\": \"W8A8_INT8 M=%lld N=%lld K=%lld\", \"kernel\": %d, \"split_k\": %d, "
                 "\"select_us\": %.4f, \"reject_us\": %.4f, \"launch_us\": %.3f, "
-                "\"empty_launch_us\": %.3f, \"graph_launch_us\": %.2f, \"graph_calls\": %d, "
+                "\"empty_launch_us\": %.3f, \"args_launch_us\": %.3f, \"graph_launch_us\": %.2f, "
+                "\"graph_calls\": %d, "
                 "\"graph_gpu_us_per_call\": %.3f}\n",
                 (long long)M, (long long)N, (long long)K, cfg.kernel, cfg.split_k, select_us,
-                reject_us, launch_us, empty_us, median(host), BURST, median(gpu));
+                reject_us, launch_us, empty_us, args_us, median(host), BURST, median(gpu));
     CK(hipGraphExecDestroy(ge));
     CK(hipGraphDestroy(g));
     return 0;

@@ -206,7 +206,9 @@ def workload(name: str):
     if name == "all_32b":
         return [(f, M, N, K) for f in FORMATS for (K, N) in SHAPES_32B
                 for M in DECODE_M + (2048,)]
+    if name == "prefill":
+        return [p for w in ("fp8_8b", "block_fp8_8b", "all_32b") for p in workload(w) if p[1] >= 512]
     raise KeyError(name)
 
 
-WORKLOADS = ("fp8_small", "int8_1p7b_decode", "fp8_8b", "block_fp8_8b", "all_32b")
+WORKLOADS = ("fp8_small", "int8_1p7b_decode", "fp8_8b", "block_fp8_8b", "all_32b", "prefill")
