@@ -536,6 +536,37 @@ k_tile(KArgs p)
                                            : mma32_piece<FMT>(af, bf[fn], j, acc[fm][fn]);
             }
         };
+        if constexpr (SCAL == SC_BLOCK) {
+            // Block scaling, software-pipelined across the 32-row A blocks:
+            // the group products of block fm+1 go to the matrix cores while
+            // the VALU promotes block fm's (acc += p * sA * sB), so the two
+            // units overlap instead of waiting on each other.
+            A16 pz[2][FN];
+            v4i af[2][4];
+            const A16 zero = {};
+            load_a(af[0], 0);
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                pz[0][fn] = SWAP ? mma32<FMT>(bf[fn], af[0], zero) : mma32<FMT>(af[0], bf[fn], zero);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int cur = fm & 1;
+                if (fm + 1 < FM) {
+                    load_a(af[cur ^ 1], fm + 1);
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+                        pz[cur ^ 1][fn] = SWAP ? mma32<FMT>(bf[fn], af[cur ^ 1], zero)
+                                               : mma32<FMT>(af[cur ^ 1], bf[fn], zero);
+                }
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    const float scale = sa[fm] * sb[fn];
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        acc[fm][fn][v] = __builtin_fmaf((float)pz[cur][fn][v], scale, (float)acc[fm][fn][v]);
+                }
+            }
+        } else {
         v4i a0[4], a1[4];
         load_a(a0, 0);
 #pragma unroll
@@ -552,6 +583,7 @@ k_tile(KArgs p)
                 block(a1, fm + 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
+        }
         }
     }
 
@@ -589,6 +621,10 @@ hipError_t launch_tile(const KArgs &a, dim3 grid, hipStream_t s)
     X(FMT, SCAL, BIT, SW, 64, 128, 1, 4, 2),          \
     X(FMT, SCAL, BIT, SW, 128, 128, 2, 2, 2),         \
     X(FMT, SCAL, BIT, SW, 128, 256, 2, 2, 2),         \
-    X(FMT, SCAL, BIT, SW, 256, 128, 2, 2, 2)
+    X(FMT, SCAL, BIT, SW, 256, 128, 2, 2, 2),         \
+    X(FMT, SCAL, BIT, SW, 256, 256, 2, 4, 2),         \
+    X(FMT, SCAL, BIT, SW, 256, 256, 4, 2, 2),         \
+    X(FMT, SCAL, BIT, SW, 256, 128, 4, 2, 2),         \
+    X(FMT, SCAL, BIT, SW, 128, 256, 2, 4, 2)
 
 }  // namespace qlin
