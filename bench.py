@@ -203,7 +203,8 @@ def prefill_points(reps: int = 4):
     timed with events on the launch stream."""
     import torch
     wl = Workload("prefill", copies_target_bytes=0)
-    wl.call(wl.items[0], 0)
+    for it in wl.items:                # eager calls size the split-K workspace before capture
+        wl.call(it, 0)
     torch.cuda.synchronize()
     out = []
     for it in wl.items:

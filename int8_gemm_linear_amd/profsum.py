@@ -131,6 +131,38 @@ def per_launch_table(folder: str, counter: str, factor: float) -> str:
     return "\n".join(lines)
 
 
+def mfma_summary(folder: str, xcds: int = 8, simds: int = 1024) -> str:
+    """Matrix-core utilisation per (GEMM kernel, grid) from a --pmc run with
+    SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and SQ_INSTS_VALU_MFMA_MOPS_*:
+    busy fraction = MFMA busy cycles / (GPU cycles x SIMDs), where the GRBM
+    count is summed over the XCDs; clock = GPU cycles / kernel duration;
+    TFLOP/s from the MOPS counters (512 operations each)."""
+    per = collections.OrderedDict()
+    for p in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(p, newline="") as f:
+            for r in csv.DictReader(f):
+                key = (p, int(r["Dispatch_Id"]))
+                d = per.setdefault(key, {"name": r["Kernel_Name"], "grid": r.get("Grid_Size", ""),
+                                         "ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    agg = collections.OrderedDict()
+    for d in per.values():
+        if not _is_gemm(d["name"]):
+            continue
+        agg.setdefault((d["name"], d["grid"]), []).append(d)
+    lines = [f"{'calls':>5} {'avg_us':>9} {'clock_GHz':>9} {'mfma_busy':>9} {'TFLOP/s':>9}  grid  kernel"]
+    for (n, g), ds in agg.items():
+        us = np.mean([d["ns"] for d in ds]) / 1e3
+        cyc = np.mean([d.get("GRBM_GUI_ACTIVE", 0.0) for d in ds]) / xcds
+        busy = np.mean([d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for d in ds])
+        mops = np.mean([d.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0) + d.get("SQ_INSTS_VALU_MFMA_MOPS_I8", 0.0)
+                        for d in ds])
+        util = busy / (cyc * simds) if cyc else float("nan")
+        lines.append(f"{len(ds):5d} {us:9.2f} {cyc / (us * 1e3):9.3f} {util:9.3f} "
+                     f"{mops * 512 / (us * 1e-6) / 1e12:9.1f}  {g}  {n[:80]}")
+    return "\n".join(lines)
+
+
 def traffic(fetch_dir: str, write_dir: str, workload: str, table: str | None) -> dict:
     out = {"workload": workload, "fingerprint": fingerprint(table)}
     for tag, folder, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
@@ -155,6 +187,8 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     t = sub.add_parser("trace")
     t.add_argument("folder")
+    m = sub.add_parser("mfma")
+    m.add_argument("folder")
     c = sub.add_parser("traffic")
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
@@ -166,6 +200,9 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         print(trace_summary(a.folder))
+        return
+    if a.cmd == "mfma":
+        print(mfma_summary(a.folder))
         return
     rec = traffic(a.fetch, a.write, a.workload, a.table)
     if a.alg_bytes_per_call:
