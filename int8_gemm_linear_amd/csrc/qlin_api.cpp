@@ -196,15 +196,24 @@ qlin_config default_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
     for (const Instance &in : registry())
         if (in.cfg.kernel == QLIN_KERNEL_TILE && (in.fmt_mask & fmt_bit(fmt, scal)))
             have_tile = true;
+    const bool tc = scal == SC_TC;
     if (M > 64 && have_tile && K % 128 == 0) {
+        // Largest tile that still gives most CUs a tile of their own; the
+        // sweep's picks at the tuned prefill points follow the same pattern
+        // (256x256 for big M*N, 128x128 at 4 stages, else 64x128 at 4 stages).
+        const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
         c.kernel = QLIN_KERNEL_TILE;
         c.variant = QLIN_SWAP_AB;          // built for all three formats
-        c.tile_m = 128;
-        c.tile_n = 128;
         c.tile_k = 128;
-        c.waves_n = 2;
-        c.waves_k = 2;
-        c.stages = 2;
+        if (tc && M >= 1024 && t128 >= 512) {
+            c.tile_m = 256, c.tile_n = 256, c.waves_n = 2, c.waves_k = 4, c.stages = 2;
+        } else if (t128 >= 192 || !tc) {
+            c.tile_m = 128, c.tile_n = 128, c.waves_n = 2, c.waves_k = 2, c.stages = tc ? 4 : 2;
+            if (!tc && t128 < 192)
+                c.tile_m = 64, c.waves_n = 1, c.waves_k = 4;
+        } else {
+            c.tile_m = 64, c.tile_n = 128, c.waves_n = 1, c.waves_k = 4, c.stages = 4;
+        }
     } else {
         // 16 weight rows per workgroup, 4 waves splitting K, 4 steps of loads
         // in flight per wave: the shape the sweep picks for most decode points.
@@ -220,11 +229,19 @@ qlin_config default_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
     int64_t gx, gy;
     grid_of(c, M, N, &gx, &gy);
     const int64_t kw = c.kernel == QLIN_KERNEL_STREAM ? c.waves_k : 1;
+    // Split K until the grid covers the CUs (tiles: half of them; a tile's
+    // workgroup holds a whole CU's LDS), keeping >= 8 K steps per split for
+    // tiles.
+    const int64_t want = c.kernel == QLIN_KERNEL_TILE ? 128 : 256;
+    const int64_t min_steps = c.kernel == QLIN_KERNEL_TILE ? 8 : 1;
     int split = 1;
-    while (gx * gy * split < 256 && split * 2 <= 256 && split * 2 * kw <= KS)
+    while (gx * gy * split < want && split * 2 <= 256 && split * 2 * kw * min_steps <= KS)
         split *= 2;
     c.split_k = split;
-    c.reduce = gx * gy <= kMaxCounters ? QLIN_REDUCE_LAST_ARRIVER : QLIN_REDUCE_TWO_PASS;
+    if (c.kernel == QLIN_KERNEL_TILE && split > 1)
+        c.reduce = QLIN_REDUCE_TWO_PASS;   // what the sweep picks for split tiles
+    else
+        c.reduce = gx * gy <= kMaxCounters ? QLIN_REDUCE_LAST_ARRIVER : QLIN_REDUCE_TWO_PASS;
     return c;
 }
 
@@ -244,7 +261,10 @@ qlin_config select_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
         if (!largest || e.M > largest->M)
             largest = &e;
     }
-    if (!best)
+    // Beyond the tuned M range the largest entry is used, unless the call is
+    // a prefill far past tables tuned only for decode (M <= 64), where a
+    // decode config would re-stream the weights once per 16-32 tokens.
+    if (!best && largest && !(M > 64 && M > 2 * largest->M))
         best = largest;
     // An entry that does not fit this M (or names an instance this build
     // lacks) falls back to the built-in default rather than failing.

@@ -56,6 +56,22 @@ __device__ inline void wait_vm_tile()
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// s_waitcnt vmcnt(L * min(n, NMAX)) for a run-time n >= 0: wait until at
+// most n steps' copies (L per step) are still in flight.
+template <int L, int NMAX>
+__device__ inline void wait_steps(int n)
+{
+    if constexpr (NMAX > 0) {
+        if (n >= NMAX) {
+            wait_vm_tile<L * NMAX>();
+            return;
+        }
+        wait_steps<L, NMAX - 1>(n);
+    } else {
+        wait_vm_tile<0>();
+    }
+}
+
 // One MFMA piece of a 128-byte K step on a 32x32 block: int8 has four
 // pieces of 16 bytes (v_mfma_i32_32x32x32_i8), e4m3 two pieces of 32 bytes
 // (v_mfma_f32_32x32x64_f8f6f4).  Same operand layout as mma32.
@@ -378,7 +394,7 @@ k_tile(KArgs p)
     constexpr int STAGE = ROWS * 128;
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
     static_assert(ROWS % 8 == 0, "rows");
-    static_assert(S >= 2 && S <= 4, "stages");
+    static_assert(S >= 2 && S <= 6 && S * STAGE <= 160 * 1024, "stages");
     static_assert(SCAL == SC_TC || S == 2, "block scaling keeps scales in a register double buffer");
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[S * STAGE];
@@ -477,13 +493,7 @@ k_tile(KArgs p)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) sb[fn] = sb_next[fn];
         }
-        const int after = min(S - 2, nst - 1 - i);      // steps issued after step i
-        if (after >= 2)
-            wait_vm_tile<L * 2>();
-        else if (after == 1)
-            wait_vm_tile<L>();
-        else
-            wait_vm_tile<0>();
+        wait_steps<L, S - 2>(nst - 1 - i);              // steps issued after step i stay in flight
         __syncthreads();
         if (i + S - 1 < nst) {
             issue(s + S - 1, (i + S - 1) % S);

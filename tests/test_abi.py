@@ -142,6 +142,20 @@ def test_default_selection_covers_all_workload_shapes():
             assert 1 <= c.split_k <= 256 and c.split_k & (c.split_k - 1) == 0
 
 
+def test_default_configs_are_valid_for_untuned_shapes():
+    # shapes outside the tuned table get the built-in choice: always a valid
+    # config, the tile kernel for prefill token counts
+    for fmt in ("fp8", "int8", "block_fp8"):
+        for M in (1, 17, 65, 128, 512, 1024, 2048, 4096):
+            for N in (128, 1152, 4224, 51328):
+                for K in (128, 1152, 4224, 25728):
+                    c = q.select_config(fmt, M, N, K)
+                    assert q.check_config(fmt, M, N, K, c) == 0, (fmt, M, N, K, c)
+                    if M > 64:
+                        assert c.kernel == q.KERNEL_TILE, (fmt, M, N, K, c)
+                        assert c.split_k == 1 or K // 128 >= 8 * c.split_k
+
+
 def test_config_table_file(tmp_path):
     c = some_stream_cfg("fp8")
     line = lambda M, split: (f"fp8 4096 2048 {M} {c.kernel} {c.variant} {c.tile_m} {c.tile_n} "
@@ -155,7 +169,10 @@ def test_config_table_file(tmp_path):
         assert q.select_config("fp8", 1, 4096, 2048).split_k == 2     # smallest tuned M >= 1
         assert q.select_config("fp8", 8, 4096, 2048).split_k == 2
         assert q.select_config("fp8", 9, 4096, 2048).split_k == 4
-        assert q.select_config("fp8", 500, 4096, 2048).split_k == 4   # beyond: the largest M
+        assert q.select_config("fp8", 64, 4096, 2048).split_k == 4    # beyond: the largest M
+        # far beyond a decode-only table (M > 64 and > 2x the largest M): the
+        # built-in prefill default, not a decode config
+        assert q.select_config("fp8", 500, 4096, 2048).kernel == q.KERNEL_TILE
         bad = tmp_path / "bad.cfg"
         bad.write_text("fp8 4096 2048 8 0 1\n")
         with pytest.raises(q.QlinError) as e:
