@@ -77,6 +77,10 @@ def _load():
     lib.orc_quant_per_token.argtypes = [I, I64, I64, P, I64, P, I64, P]
     lib.orc_quant_per_group.restype = I
     lib.orc_quant_per_group.argtypes = [I64, I64, I64, P, I64, P, I64, P]
+    lib.orc_rms_norm.restype = I
+    lib.orc_rms_norm.argtypes = [I64, I64, P, I64, P, I64, P, ctypes.c_float, P, I64]
+    lib.orc_silu_and_mul.restype = I
+    lib.orc_silu_and_mul.argtypes = [I64, I64, P, I64, P, I64]
     _lib = lib
     return lib
 
@@ -236,3 +240,51 @@ def quant_per_group(x, group: int = 128):
                                    s.ctypes.data) != 0:
         raise ValueError("oracle rejected its arguments")
     return q, s
+
+
+def rms_norm(x, w, eps: float, residual=None):
+    """RMS norm of each row of a bf16 [M,K] activation with bf16 weight [K]:
+    y = bf16((h * w) / sqrt(mean(h^2) + eps)) evaluated in double, where
+    h = x, or h = bf16(x + residual) when a residual [M,K] is given.
+    Returns (y bits [M,K], h bits [M,K] or None)."""
+    xb = _bf16_bits(x)
+    wb = _bf16_bits(w).ravel()
+    M, K = xb.shape
+    if wb.size != K:
+        raise ValueError("weight must have K elements")
+    rb = None if residual is None else _bf16_bits(residual).copy()
+    if rb is not None and rb.shape != xb.shape:
+        raise ValueError("residual must be [M,K]")
+    y = np.zeros((M, K), np.uint16)
+    if _load().orc_rms_norm(M, K, xb.ctypes.data, K, _ptr(rb), K, wb.ctypes.data,
+                            float(eps), y.ctypes.data, K) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return y, rb
+
+
+def silu_and_mul(x):
+    """SiLU-and-mul of a bf16 [M, 2K] activation (gate | up):
+    y = bf16(g / (1 + exp(-g)) * u) evaluated in double.  Returns y bits [M,K]."""
+    xb = _bf16_bits(x)
+    M, K2 = xb.shape
+    if K2 % 2:
+        raise ValueError("the activation must have 2K columns")
+    K = K2 // 2
+    y = np.zeros((M, K), np.uint16)
+    if _load().orc_silu_and_mul(M, K, xb.ctypes.data, K2, y.ctypes.data, K) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return y
+
+
+def rms_norm_quant(x, w, eps: float, fmt: int = FMT_E4M3, group: int = 0, residual=None):
+    """rms_norm followed by the dynamic quantizer (per token, or per 1 x group
+    e4m3 when ``group`` > 0).  Returns (codes, scales, residual out or None)."""
+    y, h = rms_norm(x, w, eps, residual)
+    q, s = quant_per_group(y, group) if group else quant_per_token(y, fmt)
+    return q, s, h
+
+
+def silu_and_mul_quant(x, fmt: int = FMT_E4M3, group: int = 0):
+    """silu_and_mul followed by the dynamic quantizer.  Returns (codes, scales)."""
+    y = silu_and_mul(x)
+    return quant_per_group(y, group) if group else quant_per_token(y, fmt)

@@ -414,3 +414,79 @@ int orc_quant_per_group(int64_t M, int64_t K, int64_t group, const uint16_t *x, 
                            q + m * ldq + g * group, s + m * G + g);
     return 0;
 }
+
+/* ---------------------------------------------------------------------- */
+/* Fused producers: RMS norm and SiLU-and-mul ahead of the quantizer.      */
+/* ---------------------------------------------------------------------- */
+/*
+ * "HelionがvLLMに統合 ..." (24-ai.news), section "vLLMに統合されたカーネル",
+ * items 2, 3, 6 and 7 (rms_norm_dynamic_per_token_quant,
+ * silu_and_mul_dynamic_per_token_quant, rms_norm_per_block_quant,
+ * silu_and_mul_per_block_quant), and the section on per-kernel performance
+ * that reports their speed-ups: a normalisation or gated activation fused
+ * with the dynamic quantizer above.  The pages give names only.  Readings
+ * (listed in the design doc):
+ *   - a fused kernel returns exactly what the unfused pair returns: the
+ *     producer's output is a bfloat16 activation, which the quantizer above
+ *     (per token, or per 1x128 group) then reads;
+ *   - the producer's bf16 value is its real-number result rounded once to
+ *     nearest-even, evaluated here in double:
+ *       RMS norm over a row of K:  h_k = x_k, or with a residual
+ *         h_k = bf16(x_k + r_k) (and the residual row is replaced by h);
+ *         ms = (sum_k h_k^2) / K,  inv = 1 / sqrt(ms + eps),
+ *         y_k = bf16((h_k * w_k) * inv)        (w: bf16 weight of length K);
+ *       SiLU-and-mul over a row of 2K (gate | up):
+ *         y_k = bf16((g_k / (1 + exp(-g_k))) * u_k).
+ *   Each square h_k^2 and product h_k * w_k of bf16 values is exact in
+ *   double; the sum of squares is taken for k increasing.  x_k + r_k is
+ *   exact in double unless the exponents differ by more than 45, and then
+ *   the sum lies far inside one bf16 rounding interval, so rounding it
+ *   first to double does not change its bf16 rounding.
+ */
+
+static double orc_bf16_to_double(uint16_t h) { return (double)orc_bf16_to_float(h); }
+
+/* x [M, ldx], optional residual r [M, ldr] (replaced by h), weight w [K],
+ * output y [M, ldy]; all bf16 bits.  Returns 0, or 1 on bad arguments. */
+int orc_rms_norm(int64_t M, int64_t K, const uint16_t *x, int64_t ldx, uint16_t *r, int64_t ldr,
+                 const uint16_t *w, float eps, uint16_t *y, int64_t ldy)
+{
+    if (M < 0 || K <= 0 || ldx < K || ldy < K || (r && ldr < K) || !(eps >= 0.0f))
+        return 1;
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *xr = x + m * ldx;
+        uint16_t *rr = r ? r + m * ldr : NULL;
+        uint16_t *yr = y + m * ldy;
+        double sum = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double h = orc_bf16_to_double(xr[k]);
+            if (rr) {
+                rr[k] = orc_double_to_bf16(h + orc_bf16_to_double(rr[k]));
+                h = orc_bf16_to_double(rr[k]);
+            }
+            sum += h * h;
+        }
+        const double ms = sum / (double)K;
+        const double inv = 1.0 / sqrt(ms + (double)eps);
+        for (int64_t k = 0; k < K; ++k) {
+            const double h = orc_bf16_to_double(rr ? rr[k] : xr[k]);
+            yr[k] = orc_double_to_bf16((h * orc_bf16_to_double(w[k])) * inv);
+        }
+    }
+    return 0;
+}
+
+/* x [M, ldx] holding gate columns 0..K-1 and up columns K..2K-1; y [M, ldy]. */
+int orc_silu_and_mul(int64_t M, int64_t K, const uint16_t *x, int64_t ldx, uint16_t *y,
+                     int64_t ldy)
+{
+    if (M < 0 || K <= 0 || ldx < 2 * K || ldy < K)
+        return 1;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            const double g = orc_bf16_to_double(x[m * ldx + k]);
+            const double u = orc_bf16_to_double(x[m * ldx + K + k]);
+            y[m * ldy + k] = orc_double_to_bf16((g / (1.0 + exp(-g))) * u);
+        }
+    return 0;
+}
