@@ -235,6 +235,91 @@ def prefill_points(reps: int = 4):
             "max_frac": round(float(tfs.max()) / MFMA_PEAK_TOPS, 4), "points": out}
 
 
+# Activation producers upstream of the GEMM (quantizers and fused norm /
+# activation + quantizer), at the decode (M = 32) and prefill (M = 2048)
+# sizes of the 8B- and 32B-class models: (op, M, K).  Algorithmic bytes:
+# every input and output moved once (bf16 2 B, codes 1 B, fp32 scales).
+PRODUCER_POINTS = [
+    ("quant_per_token", 32, 4096), ("quant_per_token", 2048, 5120),
+    ("quant_per_group128", 2048, 5120),
+    ("rms_norm_dynamic_per_token_quant", 32, 4096), ("rms_norm_dynamic_per_token_quant", 2048, 5120),
+    ("rms_norm_per_block_quant", 2048, 5120),
+    ("silu_and_mul_dynamic_per_token_quant", 32, 12288),
+    ("silu_and_mul_dynamic_per_token_quant", 2048, 25600),
+    ("silu_and_mul_per_block_quant", 2048, 25600),
+]
+
+
+def producer_bytes(op: str, M: int, K: int) -> int:
+    group = "group" in op or "block" in op
+    scales = 4 * M * (K // 128) if group else 4 * M
+    if op.startswith("rms_norm"):
+        return 2 * M * K * 3 + 2 * K + M * K + scales     # x, residual in/out, weight, codes
+    if op.startswith("silu"):
+        return 4 * M * K + M * K + scales                 # gate | up, codes
+    return 2 * M * K + M * K + scales
+
+
+def producer_points(reps: int = 8, target_bytes: int = 1 << 30):
+    """Per-call time of the producers: a graph of `reps` launches per point,
+    rotating over enough input copies that ~1 GiB passes between two reads
+    of the same copy (cold caches), timed with events on the launch stream."""
+    import torch
+    import int8_gemm_linear_amd as q
+    import synth
+    dev = torch.device("cuda:0")
+    out = []
+    for op, M, K in PRODUCER_POINTS:
+        cols = 2 * K if op.startswith("silu") else K
+        x0 = torch.from_numpy(synth.activations(M, cols, (51, 2, M, cols), outliers=True,
+                                                outlier_key=(51, 3, cols))).to(dev).to(torch.bfloat16)
+        nb = producer_bytes(op, M, K)
+        copies = max(2, min(64, -(-target_bytes // nb)))
+        xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+        rs = [x.clone() for x in xs] if op.startswith("rms_norm") else None
+        w = torch.from_numpy(synth.norm_weight(K, (51, 4, K))).to(dev).to(torch.bfloat16)
+        codes = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+        sc = torch.empty((M, K // 128) if ("group" in op or "block" in op) else (M,),
+                         dtype=torch.float32, device=dev)
+
+        def call(i, op=op, xs=xs, rs=rs, w=w, codes=codes, sc=sc):
+            x = xs[i % len(xs)]
+            if op == "quant_per_token":
+                q.quant_per_token(x, out=codes, scale=sc)
+            elif op == "quant_per_group128":
+                q.quant_per_group128(x, out=codes, scale=sc)
+            elif op == "rms_norm_dynamic_per_token_quant":
+                q.rms_norm_dynamic_per_token_quant(x, w, 1e-6, residual=rs[i % len(rs)], out=codes,
+                                                   scale=sc)
+            elif op == "rms_norm_per_block_quant":
+                q.rms_norm_per_block_quant(x, w, 1e-6, residual=rs[i % len(rs)], out=codes, scale=sc)
+            elif op == "silu_and_mul_dynamic_per_token_quant":
+                q.silu_and_mul_dynamic_per_token_quant(x, out=codes, scale=sc)
+            else:
+                q.silu_and_mul_per_block_quant(x, out=codes, scale=sc)
+
+        n = max(reps, copies)
+        call(0)
+        torch.cuda.synchronize()
+        g = capture(lambda: [call(i) for i in range(n)])
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / n
+        del g, xs, rs
+        gbs = nb / us / 1e3
+        out.append({"op": op, "M": M, "K": K, "us": round(us, 2), "alg_bytes": nb,
+                    "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    torch.cuda.empty_cache()
+    return {"unit": "GB/s", "peak": HBM_PEAK_GBS, "timing": "HIP-graph replay, rotating input "
+            "copies (~1 GiB between reuses), hipEvents", "points": out}
+
+
 def cpu_model() -> str:
     try:
         for ln in open("/proc/cpuinfo"):
@@ -288,6 +373,8 @@ def main():
     ap.add_argument("--per-point", action="store_true", help="print per-point timings to stderr")
     ap.add_argument("--no-dispatch", action="store_true", help="skip the host dispatch-cost run")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M >= 512 per-point timings")
+    ap.add_argument("--no-producers", action="store_true",
+                    help="skip the activation-producer timings (quantizers, fused norm / SiLU)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -362,6 +449,10 @@ def main():
     if not args.no_prefill and args.workload != "prefill":
         prefill = prefill_points()
 
+    producers = None
+    if not args.no_producers and args.workload != "prefill":
+        producers = producer_points()
+
     flops_tops = wl.flops_per_step / (ms_step * 1e-3) / 1e12
     out = {
         "metric": "effective TB/s (M<=32) and TFLOPS (M>=512) for FP8/INT8 scaled GEMM, 1 GPU",
@@ -393,6 +484,7 @@ def main():
         "cpu_baseline": cpu,
         "dispatch": dispatch,
         "prefill_mfma": prefill,
+        "producers": producers,
         "parity_vs_oracle": parity_ok,
     }
     print(json.dumps(out), flush=True)

@@ -203,6 +203,45 @@ qlin_status qlin_quant_per_token(qlin_dtype dt, int64_t M, int64_t K,
 qlin_status qlin_quant_per_group128(int64_t M, int64_t K, const uint16_t *X, int64_t ldx,
                                     void *Q, int64_t ldq, float *scale, void *stream);
 
+/* Fused producers of A: RMS norm or SiLU-and-mul followed by the quantizer
+ * above, in one pass; items 2, 3, 6 and 7 of the kernel list in
+ * "HelionがvLLMに統合 ..." (24-ai.news), section "vLLMに統合されたカーネル"
+ * (rms_norm_dynamic_per_token_quant, silu_and_mul_dynamic_per_token_quant,
+ * rms_norm_per_block_quant, silu_and_mul_per_block_quant).  The pages give
+ * names only.  Each call returns exactly what the quantizer returns on the
+ * producer's bf16 output, where that output is the real-number value
+ * rounded once to nearest-even bf16:
+ *   RMS norm of a row of K:  h = x, or h = bf16(x + residual) when residual
+ *     is not NULL (the residual row is then overwritten with h);
+ *     y_k = bf16(h_k * weight_k / sqrt(sum_j(h_j^2) / K + eps)).
+ *   SiLU-and-mul of a row of 2K values (gate in columns 0..K-1, up in
+ *     K..2K-1):  y_k = bf16(gate_k / (1 + exp(-gate_k)) * up_k).
+ * Per token: scale [M], dt e4m3 or int8.  Per block: 1x128 groups, e4m3,
+ * scale [M][K/128] row-major, K % 128 == 0.
+ *
+ * Shapes: M >= 0 (0 is a no-op), 0 < K <= 2^20, K % 16 == 0.  X [M][ldx]
+ * bf16 bits with ldx >= K (RMS norm) or >= 2K (SiLU-and-mul), ldx % 8 == 0;
+ * residual [M][ldr], ldr >= K, ldr % 8 == 0; weight [K] bf16; eps finite
+ * and > 0.  Q [M][ldq] codes, ldq >= K, ldq % 16 == 0.  X, residual,
+ * weight and Q 16-byte aligned, scale 4-byte aligned.  The caller owns every
+ * buffer; the call is asynchronous on `stream` (a hipStream_t) and allocates
+ * nothing.  Errors as for qlin_scaled_mm (bad eps: QLIN_ERR_BAD_ARGUMENT). */
+qlin_status qlin_rms_norm_dynamic_per_token_quant(qlin_dtype dt, int64_t M, int64_t K,
+                                                  const uint16_t *X, int64_t ldx,
+                                                  uint16_t *residual, int64_t ldr,
+                                                  const uint16_t *weight, float eps, void *Q,
+                                                  int64_t ldq, float *scale, void *stream);
+qlin_status qlin_rms_norm_per_block_quant(int64_t M, int64_t K, const uint16_t *X, int64_t ldx,
+                                          uint16_t *residual, int64_t ldr,
+                                          const uint16_t *weight, float eps, void *Q,
+                                          int64_t ldq, float *scale, void *stream);
+qlin_status qlin_silu_and_mul_dynamic_per_token_quant(qlin_dtype dt, int64_t M, int64_t K,
+                                                      const uint16_t *X, int64_t ldx, void *Q,
+                                                      int64_t ldq, float *scale, void *stream);
+qlin_status qlin_silu_and_mul_per_block_quant(int64_t M, int64_t K, const uint16_t *X,
+                                              int64_t ldx, void *Q, int64_t ldq, float *scale,
+                                              void *stream);
+
 /* The config the table selects for a problem: the entry for (scaling, dt,
  * N, K) at the smallest tuned M >= M (else the largest tuned M); shapes not
  * in the table get the format's default for that M range. */

@@ -135,6 +135,15 @@ def _lib():
     lib.qlin_quant_per_token.restype = I
     lib.qlin_quant_per_group128.argtypes = [I64, I64, P, I64, P, I64, P, P]
     lib.qlin_quant_per_group128.restype = I
+    F = ctypes.c_float
+    lib.qlin_rms_norm_dynamic_per_token_quant.argtypes = [I, I64, I64, P, I64, P, I64, P, F, P, I64, P, P]
+    lib.qlin_rms_norm_dynamic_per_token_quant.restype = I
+    lib.qlin_rms_norm_per_block_quant.argtypes = [I64, I64, P, I64, P, I64, P, F, P, I64, P, P]
+    lib.qlin_rms_norm_per_block_quant.restype = I
+    lib.qlin_silu_and_mul_dynamic_per_token_quant.argtypes = [I, I64, I64, P, I64, P, I64, P, P]
+    lib.qlin_silu_and_mul_dynamic_per_token_quant.restype = I
+    lib.qlin_silu_and_mul_per_block_quant.argtypes = [I64, I64, P, I64, P, I64, P, P]
+    lib.qlin_silu_and_mul_per_block_quant.restype = I
     _LIB = lib
     return lib
 
@@ -278,6 +287,109 @@ def quant_per_group128(x, out=None, scale=None):
     _call(_lib().qlin_quant_per_group128, [M, K, x.data_ptr(), ldx, out.data_ptr(), out.stride(0),
                                            scale.data_ptr(), stream.cuda_stream],
           "qlin_quant_per_group128")
+    return out, scale
+
+
+def _codes_out(out, dtype, M, K, device):
+    if out is None:
+        return torch.empty((M, K), dtype=dtype, device=device)
+    if out.dtype != dtype or tuple(out.shape) != (M, K) or out.stride(1) != 1:
+        raise ValueError(f"out must be a {dtype} [M,K] tensor with contiguous rows")
+    return out
+
+
+def _code_dtype(dtype):
+    dt = E4M3 if dtype == torch.float8_e4m3fn else (INT8 if dtype == torch.int8 else None)
+    if dt is None:
+        raise TypeError("dtype must be float8_e4m3fn or int8")
+    return dt
+
+
+def _rms_args(x, weight, residual):
+    ldx = _bf16_rows(x, "x")
+    M, K = x.shape
+    if weight.dtype != torch.bfloat16 or not weight.is_cuda or weight.dim() != 1 or weight.numel() != K or \
+            weight.stride(0) != 1:
+        raise ValueError("weight must be a contiguous bfloat16 vector of K elements")
+    ldr = 0
+    if residual is not None:
+        ldr = _bf16_rows(residual, "residual")
+        if tuple(residual.shape) != (M, K):
+            raise ValueError("residual must be [M,K]")
+    return ldx, M, K, ldr
+
+
+def rms_norm_dynamic_per_token_quant(x, weight, eps=1e-6, dtype=torch.float8_e4m3fn,
+                                     residual=None, out=None, scale=None):
+    """RMS norm of bf16 x [M,K] with bf16 weight [K] (after x += residual,
+    rounded to bf16 and written back into `residual`, when one is given),
+    then dynamic per-token quantization: returns (codes [M,K], scales [M])."""
+    ldx, M, K, ldr = _rms_args(x, weight, residual)
+    dt = _code_dtype(dtype)
+    out = _codes_out(out, dtype, M, K, x.device)
+    if scale is None:
+        scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _scale(scale, (M,), "scale")
+    stream = torch.cuda.current_stream(x.device)
+    _call(_lib().qlin_rms_norm_dynamic_per_token_quant,
+          [dt, M, K, x.data_ptr(), ldx, None if residual is None else residual.data_ptr(), ldr,
+           weight.data_ptr(), float(eps), out.data_ptr(), out.stride(0), scale.data_ptr(),
+           stream.cuda_stream], "qlin_rms_norm_dynamic_per_token_quant")
+    return out, scale
+
+
+def rms_norm_per_block_quant(x, weight, eps=1e-6, residual=None, out=None, scale=None):
+    """RMS norm as above, then per-token-group (1x128) e4m3 quantization:
+    returns (codes float8_e4m3fn [M,K], scales float32 [M, K/128])."""
+    ldx, M, K, ldr = _rms_args(x, weight, residual)
+    out = _codes_out(out, torch.float8_e4m3fn, M, K, x.device)
+    if scale is None:
+        scale = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    _scale(scale, (M, K // 128), "scale")
+    stream = torch.cuda.current_stream(x.device)
+    _call(_lib().qlin_rms_norm_per_block_quant,
+          [M, K, x.data_ptr(), ldx, None if residual is None else residual.data_ptr(), ldr,
+           weight.data_ptr(), float(eps), out.data_ptr(), out.stride(0), scale.data_ptr(),
+           stream.cuda_stream], "qlin_rms_norm_per_block_quant")
+    return out, scale
+
+
+def _silu_args(x):
+    ldx = _bf16_rows(x, "x")
+    M, K2 = x.shape
+    if K2 % 2:
+        raise ValueError("x must be [M, 2K] (gate | up)")
+    return ldx, M, K2 // 2
+
+
+def silu_and_mul_dynamic_per_token_quant(x, dtype=torch.float8_e4m3fn, out=None, scale=None):
+    """SiLU(gate) * up of bf16 x [M, 2K] (gate | up), then dynamic per-token
+    quantization: returns (codes [M,K], scales [M])."""
+    ldx, M, K = _silu_args(x)
+    dt = _code_dtype(dtype)
+    out = _codes_out(out, dtype, M, K, x.device)
+    if scale is None:
+        scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _scale(scale, (M,), "scale")
+    stream = torch.cuda.current_stream(x.device)
+    _call(_lib().qlin_silu_and_mul_dynamic_per_token_quant,
+          [dt, M, K, x.data_ptr(), ldx, out.data_ptr(), out.stride(0), scale.data_ptr(),
+           stream.cuda_stream], "qlin_silu_and_mul_dynamic_per_token_quant")
+    return out, scale
+
+
+def silu_and_mul_per_block_quant(x, out=None, scale=None):
+    """SiLU(gate) * up, then per-token-group (1x128) e4m3 quantization:
+    returns (codes float8_e4m3fn [M,K], scales float32 [M, K/128])."""
+    ldx, M, K = _silu_args(x)
+    out = _codes_out(out, torch.float8_e4m3fn, M, K, x.device)
+    if scale is None:
+        scale = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    _scale(scale, (M, K // 128), "scale")
+    stream = torch.cuda.current_stream(x.device)
+    _call(_lib().qlin_silu_and_mul_per_block_quant,
+          [M, K, x.data_ptr(), ldx, out.data_ptr(), out.stride(0), scale.data_ptr(),
+           stream.cuda_stream], "qlin_silu_and_mul_per_block_quant")
     return out, scale
 
 

@@ -23,6 +23,7 @@ SOURCES = [
     "qlin_api.cpp",
     "qlin_reduce.hip",
     "qlin_quant.hip",
+    "qlin_fused.hip",
     "qlin_stream_fp8.hip",
     "qlin_stream_int8.hip",
     "qlin_stream_block.hip",

@@ -1,0 +1,360 @@
+// Row engine of the activation producers: one workgroup of W waves per token
+// row produces the row's bf16 activation (a copy of the input, an RMS norm,
+// or SiLU-and-mul) and quantizes it (per token, or per 1x128 group).
+//
+// These kernels are HBM-bound: per value 2 bytes in (4 for SiLU-and-mul,
+// +4 for a residual read and written back) and 1 byte out.  What keeps them
+// at the bandwidth is latency hiding, so a row is as few waves as fit it in
+// registers (W = 1 for rows up to 4096 values, 2 up to 8192, ... 8 up to
+// 32768): every lane issues all its 16-byte loads (kReg pieces) before it
+// uses any, a single-wave row reduces with shuffles alone, and small
+// workgroups let many rows be in flight per CU.  Lane t of the row owns the
+// pieces t, t + 64W, ...; pieces beyond the register window (rows longer
+// than 32768) are produced again from the L2-resident input in the
+// quantizer's second pass.  Per-group scaling needs no row reduction: the
+// 16 lanes of one 128-value group are consecutive (64W is a multiple of 16).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "qlin_quant.h"
+
+namespace qlin {
+namespace rows {
+
+using namespace quant;
+
+enum { OP_QUANT = 0, OP_RMS = 1, OP_SILU = 2 };
+enum { Q_TOKEN_E4M3 = 0, Q_TOKEN_INT8 = 1, Q_GROUP_E4M3 = 2 };
+constexpr int kReg = 8;          // 16-byte pieces per lane held in registers
+constexpr int kMaxW = 8;
+
+struct RowArgs {
+    const uint16_t *X;           // [M][ldx] bf16 (SiLU: gate | up, 2K values)
+    int64_t ldx;
+    uint16_t *R;                 // residual [M][ldr] (RMS norm, may be null)
+    int64_t ldr;
+    const uint16_t *Wt;          // RMS weight [K]
+    float eps;
+    uint8_t *Q;                  // codes [M][ldq]
+    int64_t ldq;
+    float *S;                    // scales [M] or [M][K/128]
+    int K;
+};
+
+// double -> bf16 bits, nearest-even, one rounding: truncation to fp32 with
+// the inexact bit kept in the last place (round to odd; 24 >= 8 + 2 bits),
+// then nearest-even to bf16.
+__device__ inline uint32_t bf16_of_double(double d)
+{
+    const float f = __double2float_rz(d);
+    uint32_t u = __float_as_uint(f);
+    if ((double)f != d)
+        u |= 1u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ inline double dlo(uint32_t w) { return (double)bf16_lo(w); }
+__device__ inline double dhi(uint32_t w) { return (double)bf16_hi(w); }
+__device__ inline uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
+
+// h = bf16(x + r) for 8 values.
+__device__ inline u32x4 add_round8(u32x4 x, u32x4 r)
+{
+    u32x4 h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        h[j] = pack2(bf16_of_double(dlo(x[j]) + dlo(r[j])), bf16_of_double(dhi(x[j]) + dhi(r[j])));
+    return h;
+}
+
+__device__ inline double sumsq8(u32x4 h, double acc)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        acc = fma(dlo(h[j]), dlo(h[j]), acc);
+        acc = fma(dhi(h[j]), dhi(h[j]), acc);
+    }
+    return acc;
+}
+
+// y = bf16((h * w) * inv) for 8 values (h * w is exact in double).
+__device__ inline u32x4 norm8(u32x4 h, u32x4 w, double inv)
+{
+    u32x4 y;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        y[j] = pack2(bf16_of_double((dlo(h[j]) * dlo(w[j])) * inv),
+                     bf16_of_double((dhi(h[j]) * dhi(w[j])) * inv));
+    return y;
+}
+
+// bf16(g / (1 + e^-g) * u), the real value rounded once, for 8 values.
+// Fast path in fp32 for |g| <= 64: p = -g log2(e) carried as p_hi + p_lo
+// (p_lo from an fma: the argument is exact to ~2^-48), e^-g = 2^p_hi *
+// (1 + p_lo ln 2) with the hardware exp2 (~1 ulp), then 1 + t, the hardware
+// reciprocal (~1 ulp) and two products: with a few ulp allowed per hardware
+// step, y32 is within 2^-20 (16 ulp) of the real value.  When every
+// intermediate is a normal fp32 number and y32's low 16 bits are more than
+// 64 ulp from the bf16 tie pattern 0x8000, no bf16 rounding boundary lies
+// between y32 and the real value, so rounding y32 gives the same bf16.  The
+// other values (about 0.2%, and |g| > 64 where e^-g leaves fp32) are
+// computed in double (library exp, correctly rounded division) and rounded
+// once.
+// Out of line: rare, and inlined at every value it would multiply the code size.
+__device__ __attribute__((noinline)) uint32_t silu_exact(float g, float u)
+{
+    const double gd = g;
+    return bf16_of_double((gd / (1.0 + exp(-gd))) * (double)u);
+}
+
+__device__ inline u32x4 silu8(u32x4 gw, u32x4 uw)
+{
+    constexpr float L_HI = 1.44269502162933349609375f;          // log2(e) rounded to fp32
+    constexpr float L_LO = 1.925962989e-8f;                     // log2(e) - L_HI
+    constexpr float LN2 = 0.693147180559945309f;
+    float g[8], u[8];
+    uint32_t b[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        g[2 * j] = bf16_lo(gw[j]);
+        g[2 * j + 1] = bf16_hi(gw[j]);
+        u[2 * j] = bf16_lo(uw[j]);
+        u[2 * j + 1] = bf16_hi(uw[j]);
+    }
+    uint32_t need = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float ng = -g[j];
+        const float p_hi = ng * L_HI;
+        const float p_lo = fmaf(ng, L_HI, -p_hi) + ng * L_LO;
+        const float t = __builtin_amdgcn_exp2f(p_hi) * fmaf(p_lo, LN2, 1.0f);
+        const float sv = g[j] * __builtin_amdgcn_rcpf(1.0f + t);
+        const float y = sv * u[j];
+        const float as = fabsf(sv), ay = fabsf(y);
+        const uint32_t bits = __float_as_uint(y);
+        const bool ok = fabsf(g[j]) <= 64.0f && as >= 0x1p-100f && ay >= 0x1p-100f &&
+                        ay <= 0x1p+100f && ((bits & 0xFFFFu) - 0x7FC0u) >= 128u;
+        need |= ok ? 0u : 1u << j;
+        b[j] = (bits + 0x7FFFu + ((bits >> 16) & 1u)) >> 16;
+    }
+    if (need) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (need & (1u << j))
+                b[j] = silu_exact(g[j], u[j]);
+    }
+    u32x4 y;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        y[j] = pack2(b[2 * j], b[2 * j + 1]);
+    return y;
+}
+
+// Sum / maximum over the row's W waves (every lane gets the result).
+template <int W>
+__device__ inline double row_sum(double v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    if constexpr (W > 1) {
+        __shared__ double red[kMaxW];
+        if ((threadIdx.x & 63) == 0)
+            red[threadIdx.x >> 6] = v;
+        __syncthreads();
+        v = red[0];
+#pragma unroll
+        for (int w = 1; w < W; ++w)
+            v += red[w];
+    }
+    return v;
+}
+
+template <int W>
+__device__ inline float row_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, 64));
+    if constexpr (W > 1) {
+        __shared__ float red[kMaxW];
+        if ((threadIdx.x & 63) == 0)
+            red[threadIdx.x >> 6] = v;
+        __syncthreads();
+        v = red[0];
+#pragma unroll
+        for (int w = 1; w < W; ++w)
+            v = fmaxf(v, red[w]);
+    }
+    return v;
+}
+
+// Quantizes the row: pieces of the register window in `y`, the rest
+// produced again by redo(p).
+template <int QM, int W, class Redo>
+__device__ inline void quantize_row(const u32x4 (&y)[kReg], int P, uint8_t *qrow, float *srow,
+                                    Redo redo)
+{
+    constexpr int NT = 64 * W;
+    uint2 *q = reinterpret_cast<uint2 *>(qrow);
+    const int t = threadIdx.x;
+    if constexpr (QM == Q_GROUP_E4M3) {
+        // P is a multiple of 16: the 16 lanes of a group are all active or
+        // all idle, so the 16-wide butterfly stays inside the group
+        auto emit = [&](const u32x4 &v, int p) {
+            float m = amax8(v);
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1)
+                m = fmaxf(m, __shfl_xor(m, o, 16));
+            const float s = span_scale<false>(m);
+            q[p] = quant8<false>(v, s);
+            if ((t & 15) == 0)
+                srow[p >> 4] = s;
+        };
+#pragma unroll
+        for (int i = 0; i < kReg; ++i) {
+            const int p = t + i * NT;
+            if (p < P)
+                emit(y[i], p);
+        }
+        for (int p = t + kReg * NT; p < P; p += NT)
+            emit(redo(p), p);
+    } else {
+        constexpr bool INT8 = QM == Q_TOKEN_INT8;
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kReg; ++i)
+            m = fmaxf(m, amax8(y[i]));
+        for (int p = t + kReg * NT; p < P; p += NT)
+            m = fmaxf(m, amax8(redo(p)));
+        const float s = span_scale<INT8>(row_max<W>(m));
+        if (t == 0)
+            srow[0] = s;
+#pragma unroll
+        for (int i = 0; i < kReg; ++i) {
+            const int p = t + i * NT;
+            if (p < P)
+                q[p] = quant8<INT8>(y[i], s);
+        }
+        for (int p = t + kReg * NT; p < P; p += NT)
+            q[p] = quant8<INT8>(redo(p), s);
+    }
+}
+
+template <int OP, int QM, int W, bool RES>
+__global__ void __launch_bounds__(64 * W)
+k_rows(RowArgs a)
+{
+    constexpr int NT = 64 * W;
+    const int row = blockIdx.x;
+    const int t = threadIdx.x;
+    const int P = a.K >> 3;
+    const u32x4 *x = reinterpret_cast<const u32x4 *>(a.X + (int64_t)row * a.ldx);
+    uint8_t *qrow = a.Q + (int64_t)row * a.ldq;
+    float *srow = a.S + (QM == Q_GROUP_E4M3 ? (int64_t)row * (a.K >> 7) : (int64_t)row);
+    const u32x4 zero = {0, 0, 0, 0};
+    u32x4 y[kReg];
+
+    if constexpr (OP == OP_QUANT) {
+#pragma unroll
+        for (int i = 0; i < kReg; ++i) {
+            const int p = t + i * NT;
+            y[i] = p < P ? __builtin_nontemporal_load(x + p) : zero;
+        }
+        quantize_row<QM, W>(y, P, qrow, srow, [&](int p) { return x[p]; });
+    } else if constexpr (OP == OP_SILU) {
+        const u32x4 *u = x + P;                     // up half of the row
+        u32x4 gu[kReg];
+#pragma unroll
+        for (int i = 0; i < kReg; ++i) {
+            const int p = t + i * NT;
+            y[i] = p < P ? __builtin_nontemporal_load(x + p) : zero;
+            gu[i] = p < P ? __builtin_nontemporal_load(u + p) : zero;
+        }
+#pragma unroll
+        for (int i = 0; i < kReg; ++i)
+            y[i] = silu8(y[i], gu[i]);
+        quantize_row<QM, W>(y, P, qrow, srow, [&](int p) { return silu8(x[p], u[p]); });
+    } else {
+        u32x4 *r = RES ? reinterpret_cast<u32x4 *>(a.R + (int64_t)row * a.ldr) : nullptr;
+        const u32x4 *w = reinterpret_cast<const u32x4 *>(a.Wt);
+        u32x4 rr[kReg];
+#pragma unroll
+        for (int i = 0; i < kReg; ++i) {
+            const int p = t + i * NT;
+            y[i] = p < P ? __builtin_nontemporal_load(x + p) : zero;
+            if (RES)
+                rr[i] = p < P ? r[p] : zero;
+        }
+        // h (the residual row replaced by it) and the sum of its squares
+        double acc = 0.0;
+#pragma unroll
+        for (int i = 0; i < kReg; ++i) {
+            const int p = t + i * NT;
+            if (RES && p < P) {
+                y[i] = add_round8(y[i], rr[i]);
+                r[p] = y[i];
+            }
+            acc = sumsq8(y[i], acc);
+        }
+        for (int p = t + kReg * NT; p < P; p += NT) {
+            u32x4 h = x[p];
+            if (RES) {
+                h = add_round8(h, r[p]);
+                r[p] = h;
+            }
+            acc = sumsq8(h, acc);
+        }
+        const double inv = 1.0 / sqrt(row_sum<W>(acc) / (double)a.K + (double)a.eps);
+#pragma unroll
+        for (int i = 0; i < kReg; ++i) {
+            const int p = t + i * NT;
+            if (p < P)
+                y[i] = norm8(y[i], w[p], inv);
+        }
+        // beyond the register window h is re-read (the residual row holds it)
+        quantize_row<QM, W>(y, P, qrow, srow,
+                            [&](int p) { return norm8(RES ? r[p] : x[p], w[p], inv); });
+    }
+}
+
+// Waves per row: the fewest that hold the row's pieces in registers.
+inline int waves_for(int64_t K)
+{
+    const int64_t P = K >> 3;
+    int w = 1;
+    while (w < kMaxW && (int64_t)64 * w * kReg < P)
+        w *= 2;
+    return w;
+}
+
+template <int OP, int QM, bool RES>
+hipError_t launch_rows(const RowArgs &a, int64_t M, hipStream_t s)
+{
+    const dim3 grid((unsigned)M);
+    switch (waves_for(a.K)) {
+    case 1: hipLaunchKernelGGL((k_rows<OP, QM, 1, RES>), grid, dim3(64), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_rows<OP, QM, 2, RES>), grid, dim3(128), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_rows<OP, QM, 4, RES>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_rows<OP, QM, 8, RES>), grid, dim3(512), 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+// Launch with the scaling mode chosen at run time.
+template <int OP, bool RES>
+hipError_t launch_rows_qm(int qm, const RowArgs &a, int64_t M, hipStream_t s)
+{
+    if (qm == Q_TOKEN_INT8)
+        return launch_rows<OP, Q_TOKEN_INT8, RES>(a, M, s);
+    if (qm == Q_TOKEN_E4M3)
+        return launch_rows<OP, Q_TOKEN_E4M3, RES>(a, M, s);
+    return launch_rows<OP, Q_GROUP_E4M3, RES>(a, M, s);
+}
+
+}  // namespace rows
+}  // namespace qlin

@@ -105,6 +105,12 @@ def activations(M: int, K: int, key, outliers: bool = False, outlier_key=None) -
     return bf16_round(x)
 
 
+def norm_weight(K: int, key) -> np.ndarray:
+    """bf16-valued RMS-norm weight [K] ~ 1 + N(0, 0.1) (a trained norm's gains
+    sit near 1)."""
+    return bf16_round((1.0 + 0.1 * rng(*key).standard_normal(K)).astype(np.float32))
+
+
 def weights(N: int, K: int, key) -> np.ndarray:
     """bf16-valued weights ~ N(0, 0.02)."""
     g = key if isinstance(key, np.random.Generator) else rng(*key)

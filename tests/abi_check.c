@@ -22,6 +22,7 @@ int main(void)
     const void *A = (const void *)0x10000, *B = (const void *)0x20000;
     void *Y = (void *)0x30000;
     const float *s = (const float *)0x40000;
+    float *so = (float *)0x40000;
     qlin_config c;
 
     expect("abi version", qlin_abi_version() == QLINEAR_ABI_VERSION ? QLIN_OK : QLIN_ERR_HIP, QLIN_OK);
@@ -63,6 +64,17 @@ int main(void)
     expect("workspace size > 0",
            qlin_workspace_size(QLIN_TOKEN_CHANNEL, QLIN_INT8, 16, 4096, 2048, &c) > 0 ? QLIN_OK : QLIN_ERR_WORKSPACE,
            QLIN_OK);
+    expect("fused rms norm: K % 16",
+           qlin_rms_norm_dynamic_per_token_quant(QLIN_E4M3, 4, 40, A, 48, NULL, 0, B, 1e-6f, Y, 48, so, NULL),
+           QLIN_ERR_BAD_SHAPE);
+    expect("fused rms norm per block: K % 128",
+           qlin_rms_norm_per_block_quant(4, 144, A, 144, NULL, 0, B, 1e-6f, Y, 144, so, NULL),
+           QLIN_ERR_BAD_SHAPE);
+    expect("fused silu: rows of 2K",
+           qlin_silu_and_mul_dynamic_per_token_quant(QLIN_INT8, 4, 64, A, 64, Y, 64, so, NULL),
+           QLIN_ERR_BAD_STRIDE);
+    expect("fused silu per block: empty",
+           qlin_silu_and_mul_per_block_quant(0, 128, NULL, 256, NULL, 128, NULL, NULL), QLIN_OK);
     expect("missing table file", qlin_load_config_table("/nonexistent/qlin.cfg"), QLIN_ERR_CONFIG_FILE);
     expect("restore compiled-in table", qlin_load_config_table(NULL), QLIN_OK);
     qlin_config k0;

@@ -238,3 +238,51 @@ def test_quant_validation_errors():
     assert qtok(X=A16 + 8) == ST["align"]
     assert qgrp(Q=B16 + 4) == ST["align"]
     assert qtok(S=S4 + 2) == ST["align"]
+
+
+def frms(dt=q.E4M3, M=4, K=1024, X=A16, ldx=None, R=None, ldr=0, W=B16, eps=1e-6, Q=B16,
+         ldq=None, S=S4, block=False):
+    lib = q.lib()
+    if block:
+        return lib.qlin_rms_norm_per_block_quant(M, K, X, K if ldx is None else ldx, R, ldr, W,
+                                                 eps, Q, K if ldq is None else ldq, S, None)
+    return lib.qlin_rms_norm_dynamic_per_token_quant(dt, M, K, X, K if ldx is None else ldx, R, ldr,
+                                                     W, eps, Q, K if ldq is None else ldq, S, None)
+
+
+def fsilu(dt=q.E4M3, M=4, K=1024, X=A16, ldx=None, Q=B16, ldq=None, S=S4, block=False):
+    lib = q.lib()
+    ldx = 2 * K if ldx is None else ldx
+    if block:
+        return lib.qlin_silu_and_mul_per_block_quant(M, K, X, ldx, Q, K if ldq is None else ldq,
+                                                     S, None)
+    return lib.qlin_silu_and_mul_dynamic_per_token_quant(dt, M, K, X, ldx, Q,
+                                                         K if ldq is None else ldq, S, None)
+
+
+def test_fused_producer_validation_errors():
+    # argument checks return before any launch (no GPU needed)
+    assert frms(dt=7) == ST["arg"]
+    assert fsilu(dt=7) == ST["arg"]
+    assert frms(K=24) == ST["shape"]
+    assert frms(K=1040, block=True) == ST["shape"]          # 1x128 groups need K % 128
+    assert fsilu(K=1040, block=True) == ST["shape"]
+    assert frms(M=-1) == ST["shape"]
+    assert fsilu(K=1 << 20) == ST["shape"]                  # 2K columns past the limit
+    assert frms(M=0, X=None, W=None, Q=None, S=None) == ST["ok"]
+    assert fsilu(M=0, X=None, Q=None, S=None) == ST["ok"]
+    assert frms(W=None) == ST["null"]
+    assert frms(X=None) == ST["null"]
+    assert fsilu(S=None, block=True) == ST["null"]
+    assert frms(ldx=1000) == ST["stride"]
+    assert fsilu(ldx=2040) == ST["stride"]                  # rows of 2K values
+    assert frms(R=A16, ldr=1000) == ST["stride"]
+    assert frms(R=A16, ldr=1028) == ST["stride"]
+    assert frms(ldq=1032) == ST["stride"]
+    assert frms(W=B16 + 8) == ST["align"]
+    assert frms(R=A16 + 8, ldr=1024) == ST["align"]
+    assert fsilu(X=A16 + 8) == ST["align"]
+    assert frms(eps=-1.0) == ST["arg"]
+    assert frms(eps=0.0) == ST["arg"]
+    assert frms(eps=float("inf")) == ST["arg"]
+    assert frms(eps=float("nan")) == ST["arg"]
