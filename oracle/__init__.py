@@ -288,3 +288,33 @@ def silu_and_mul_quant(x, fmt: int = FMT_E4M3, group: int = 0):
     """silu_and_mul followed by the dynamic quantizer.  Returns (codes, scales)."""
     y = silu_and_mul(x)
     return quant_per_group(y, group) if group else quant_per_token(y, fmt)
+
+
+def grouped_scaled_mm(fmt: int, offsets, A, sA, B, sB, *, block: bool = False,
+                      max_rows: int | None = None, Y=None, nthreads: int = 0):
+    """Grouped (mixture-of-experts) product: for each group g, rows
+    offsets[g] .. offsets[g+1]-1 of A / sA times B[g]^T with scales sB[g],
+    each exactly the single product on that slice (``scaled_mm``).  Rows of a
+    group past ``max_rows`` are not computed: they keep the values of ``Y``
+    (bf16 bits [rows, N], zeros when not given).  Returns Y."""
+    offsets = np.asarray(offsets, np.int64)
+    A = _u8(A)
+    B = _u8(B)
+    G, N, K = B.shape
+    rows = A.shape[0]
+    if offsets.shape != (G + 1,) or offsets[0] != 0 or np.any(np.diff(offsets) < 0) or \
+            offsets[-1] > rows:
+        raise ValueError("offsets must be G+1 nondecreasing row offsets from 0")
+    Y = np.zeros((rows, N), np.uint16) if Y is None else np.array(Y, np.uint16, copy=True)
+    sA = np.asarray(sA, np.float32)
+    sB = np.asarray(sB, np.float32)
+    for g in range(G):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        if max_rows is not None:
+            hi = min(hi, lo + int(max_rows))
+        if hi <= lo:
+            continue
+        r = scaled_mm(fmt, A[lo:hi], sA[lo:hi], B[g], sB[g], block=block, nthreads=nthreads,
+                      want_extra=False)
+        Y[lo:hi] = r.y
+    return Y
