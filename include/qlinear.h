@@ -170,6 +170,44 @@ qlin_status qlin_block_scaled_mm_cfg(int64_t M, int64_t N, int64_t K,
                                      void *workspace, size_t workspace_bytes, void *stream,
                                      const qlin_config *cfg);
 
+/* Grouped GEMM for mixture-of-experts layers: `groups` independent
+ * scaled_mm / block_scaled_mm problems sharing N and K, in one launch.  The
+ * ai-radar commentary "Helion in vLLM: il tuning dei GEMM diventa ricerca…",
+ * section "Oltre Hopper: Blackwell, AMD, TPU e il perimetro del fork", names
+ * MoE as the next target: many experts with few tokens each, where the
+ * Split-K / Swap-AB choice matters more.  Reading: group g (an expert) owns
+ * the rows group_offsets[g] .. group_offsets[g+1]-1 of A, a_scale and Y
+ * (tokens sorted by expert) and its own weights B_g = B + g * b_group_stride
+ * bytes with scales b_scale + g * b_scale_group_stride floats; each group's
+ * result is exactly that of the single call on its slice.
+ *
+ * group_offsets: groups + 1 nondecreasing int32 values in DEVICE memory,
+ * group_offsets[0] = 0 (the call reads them on the GPU, so routing computed
+ * on the device needs no host round trip).  max_rows: a bound on any
+ * group's row count (host value): the grid covers max_rows rows per group,
+ * and rows of a group beyond max_rows are not computed.  A, a_scale and Y
+ * must hold group_offsets[groups] rows.  Per-group layouts and scales as in
+ * qlin_scaled_mm (token/channel) or qlin_block_scaled_mm (b_scale of a
+ * group [N/128][K/128]).  b_group_stride % 16 == 0, both strides >= 0.
+ * groups <= 65535 (0 is a no-op).  The config (NULL: the table's choice
+ * for (N, K) at M = max_rows) runs with split_k = 1: the groups fill the
+ * machine, grid.z carries the group, and no workspace is used; a config
+ * with split_k > 1 is rejected.  Empty groups cost one early-exiting
+ * workgroup per tile.  Asynchronous on `stream`; allocates nothing; errors
+ * as for qlin_scaled_mm (the offsets are not checked on the host). */
+qlin_status qlin_grouped_scaled_mm(qlin_dtype dt, int64_t groups, const int32_t *group_offsets,
+                                   int64_t max_rows, int64_t N, int64_t K, const void *A,
+                                   int64_t lda, const float *a_scale, const void *B, int64_t ldb,
+                                   int64_t b_group_stride, const float *b_scale,
+                                   int64_t b_scale_group_stride, void *Y, int64_t ldy, void *stream,
+                                   const qlin_config *cfg);
+qlin_status qlin_grouped_block_scaled_mm(int64_t groups, const int32_t *group_offsets,
+                                         int64_t max_rows, int64_t N, int64_t K, const void *A,
+                                         int64_t lda, const float *a_scale, const void *B,
+                                         int64_t ldb, int64_t b_group_stride, const float *b_scale,
+                                         int64_t b_scale_group_stride, void *Y, int64_t ldy,
+                                         void *stream, const qlin_config *cfg);
+
 /* Test hook: the raw int32 dot products acc[M][ldacc] = A * B^T of W8A8_INT8
  * with the given config (NULL: the table's), no scaling, no rounding. */
 qlin_status qlin_int8_accumulate(int64_t M, int64_t N, int64_t K,

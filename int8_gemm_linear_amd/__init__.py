@@ -136,6 +136,12 @@ def _lib():
     lib.qlin_quant_per_group128.argtypes = [I64, I64, P, I64, P, I64, P, P]
     lib.qlin_quant_per_group128.restype = I
     F = ctypes.c_float
+    lib.qlin_grouped_scaled_mm.argtypes = [I, I64, P, I64, I64, I64, P, I64, P, P, I64, I64, P, I64,
+                                           P, I64, P, CP]
+    lib.qlin_grouped_scaled_mm.restype = I
+    lib.qlin_grouped_block_scaled_mm.argtypes = [I64, P, I64, I64, I64, P, I64, P, P, I64, I64, P,
+                                                 I64, P, I64, P, CP]
+    lib.qlin_grouped_block_scaled_mm.restype = I
     lib.qlin_rms_norm_dynamic_per_token_quant.argtypes = [I, I64, I64, P, I64, P, I64, P, F, P, I64, P, P]
     lib.qlin_rms_norm_dynamic_per_token_quant.restype = I
     lib.qlin_rms_norm_per_block_quant.argtypes = [I64, I64, P, I64, P, I64, P, F, P, I64, P, P]
@@ -422,6 +428,67 @@ def block_scaled_mm(a_q, a_scale, b_q, b_scale, out=None, config: Config | None 
         _call(_lib().qlin_block_scaled_mm, args, "qlin_block_scaled_mm")
     else:
         _call(_lib().qlin_block_scaled_mm_cfg, args + [ctypes.byref(c)], "qlin_block_scaled_mm_cfg")
+    return out
+
+
+def _grouped_args(a_q, b_q, group_offsets, out):
+    if b_q.dim() != 3 or b_q.stride(2) != 1 or not b_q.is_cuda:
+        raise ValueError("b_q must be a [G,N,K] device tensor with contiguous rows")
+    G, N, K = b_q.shape
+    lda = _rows(a_q, "a_q")
+    if a_q.shape[1] != K:
+        raise ValueError("A is [rows,K] and B must be [G,N,K]")
+    if group_offsets.dtype != torch.int32 or group_offsets.dim() != 1 or \
+            group_offsets.numel() != G + 1 or not group_offsets.is_cuda or \
+            not group_offsets.is_contiguous():
+        raise ValueError("group_offsets must be a contiguous int32 device tensor of G+1 values")
+    rows = a_q.shape[0]
+    if out is None:
+        out = torch.empty((rows, N), dtype=torch.bfloat16, device=a_q.device)
+    elif out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1 or \
+            tuple(out.shape) != (rows, N):
+        raise ValueError("out must be a bf16 [rows,N] tensor with contiguous rows")
+    return G, N, K, lda, rows, out
+
+
+def grouped_scaled_mm(a_q, a_scale, b_q, b_scale, group_offsets, max_rows: int, out=None,
+                      config: Config | None = None):
+    """Grouped (mixture-of-experts) FP8_Dynamic / W8A8_INT8: expert g computes
+    rows group_offsets[g] .. group_offsets[g+1]-1 of A [rows,K] against its
+    weights b_q[g] [N,K] with scales b_scale[g] [N]; bf16 out [rows,N].
+    max_rows bounds any expert's row count."""
+    dt = _dt(a_q)
+    if b_q.dtype != a_q.dtype:
+        raise TypeError("A and B must have the same dtype")
+    G, N, K, lda, rows, out = _grouped_args(a_q, b_q, group_offsets, out)
+    _scale(a_scale, (rows,), "a_scale")
+    _scale(b_scale, (G, N), "b_scale")
+    c = config._c() if config is not None else None
+    stream = torch.cuda.current_stream(a_q.device)
+    _call(_lib().qlin_grouped_scaled_mm,
+          [dt, G, group_offsets.data_ptr(), int(max_rows), N, K, a_q.data_ptr(), lda,
+           a_scale.data_ptr(), b_q.data_ptr(), b_q.stride(1), b_q.stride(0), b_scale.data_ptr(), N,
+           out.data_ptr(), out.stride(0), stream.cuda_stream, ctypes.byref(c) if c else None],
+          "qlin_grouped_scaled_mm")
+    return out
+
+
+def grouped_block_scaled_mm(a_q, a_scale, b_q, b_scale, group_offsets, max_rows: int, out=None,
+                            config: Config | None = None):
+    """Grouped Block_FP8: as grouped_scaled_mm with a_scale [rows, K/128] and
+    b_scale [G, N/128, K/128]."""
+    if a_q.dtype != torch.float8_e4m3fn or b_q.dtype != torch.float8_e4m3fn:
+        raise TypeError("grouped_block_scaled_mm takes float8_e4m3fn operands")
+    G, N, K, lda, rows, out = _grouped_args(a_q, b_q, group_offsets, out)
+    _scale(a_scale, (rows, K // 128), "a_scale")
+    _scale(b_scale, (G, N // 128, K // 128), "b_scale")
+    c = config._c() if config is not None else None
+    stream = torch.cuda.current_stream(a_q.device)
+    _call(_lib().qlin_grouped_block_scaled_mm,
+          [G, group_offsets.data_ptr(), int(max_rows), N, K, a_q.data_ptr(), lda,
+           a_scale.data_ptr(), b_q.data_ptr(), b_q.stride(1), b_q.stride(0), b_scale.data_ptr(),
+           (N // 128) * (K // 128), out.data_ptr(), out.stride(0), stream.cuda_stream,
+           ctypes.byref(c) if c else None], "qlin_grouped_block_scaled_mm")
     return out
 
 

@@ -350,7 +350,24 @@ qlin_status run(const Problem &pb, const qlin_config *cfg_in)
     if (pb.M == 0 || pb.N == 0)
         return cfg_in ? (find_instance(pb.fmt, pb.scal, *cfg_in) ? QLIN_OK : QLIN_ERR_BAD_CONFIG)
                       : QLIN_OK;
-    const qlin_config cfg = cfg_in ? *cfg_in : select_config(pb.fmt, pb.scal, pb.M, pb.N, pb.K);
+    const bool grouped = pb.groups > 0;
+    if (grouped) {
+        if (pb.groups > 65535)
+            return QLIN_ERR_BAD_SHAPE;
+        if (!pb.group_off)
+            return QLIN_ERR_NULL_POINTER;
+        if (!aligned(pb.group_off, 4))
+            return QLIN_ERR_MISALIGNED;
+        if (pb.b_gstride < 0 || pb.b_gstride % 16 || pb.sb_gstride < 0)
+            return QLIN_ERR_BAD_STRIDE;
+        if (cfg_in && cfg_in->split_k != 1)
+            return QLIN_ERR_BAD_CONFIG;   // grid.z carries the group
+    }
+    qlin_config cfg = cfg_in ? *cfg_in : select_config(pb.fmt, pb.scal, pb.M, pb.N, pb.K);
+    if (grouped && !cfg_in) {
+        cfg.split_k = 1;                  // the groups fill the machine instead
+        cfg.reduce = QLIN_REDUCE_LAST_ARRIVER;
+    }
     const Instance *inst = nullptr;
     st = check_config(pb.fmt, pb.scal, pb.M, pb.N, pb.K, cfg, &inst);
     if (st != QLIN_OK)
@@ -394,9 +411,14 @@ qlin_status run(const Problem &pb, const qlin_config *cfg_in)
         a.counters = static_cast<int32_t *>(pb.ws);
         a.part = static_cast<char *>(pb.ws) + kCounterBytes;
     }
+    if (grouped) {
+        a.group_off = pb.group_off;
+        a.b_gstride = pb.b_gstride;
+        a.sb_gstride = pb.sb_gstride;
+    }
     int64_t gx, gy;
     grid_of(cfg, pb.M, pb.N, &gx, &gy);
-    const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)cfg.split_k);
+    const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)(grouped ? pb.groups : cfg.split_k));
     hipError_t e = inst->fn(a, grid, pb.stream);
     if (e == hipSuccess && cfg.split_k > 1 && cfg.reduce == QLIN_REDUCE_TWO_PASS)
         e = launch_reduce(pb.fmt, pb.scal, a, pb.stream);
@@ -473,6 +495,49 @@ qlin_status qlin_block_scaled_mm(int64_t M, int64_t N, int64_t K, const void *A,
 {
     return qlin_block_scaled_mm_cfg(M, N, K, A, lda, a_scale, B, ldb, b_scale, Y, ldy, workspace,
                                     workspace_bytes, stream, nullptr);
+}
+
+qlin_status qlin_grouped_scaled_mm(qlin_dtype dt, int64_t groups, const int32_t *group_offsets,
+                                   int64_t max_rows, int64_t N, int64_t K, const void *A,
+                                   int64_t lda, const float *a_scale, const void *B, int64_t ldb,
+                                   int64_t b_group_stride, const float *b_scale,
+                                   int64_t b_scale_group_stride, void *Y, int64_t ldy, void *stream,
+                                   const qlin_config *cfg)
+{
+    const int fmt = fmt_of(dt);
+    if (fmt < 0)
+        return QLIN_ERR_BAD_ARGUMENT;
+    if (groups < 0)
+        return QLIN_ERR_BAD_SHAPE;
+    if (groups == 0)
+        return QLIN_OK;
+    Problem pb = make_problem(fmt, SC_TC, max_rows, N, K, A, lda, a_scale, B, ldb, b_scale, Y, ldy,
+                              nullptr, 0, stream);
+    pb.groups = groups;
+    pb.group_off = group_offsets;
+    pb.b_gstride = b_group_stride;
+    pb.sb_gstride = b_scale_group_stride;
+    return run(pb, cfg);
+}
+
+qlin_status qlin_grouped_block_scaled_mm(int64_t groups, const int32_t *group_offsets,
+                                         int64_t max_rows, int64_t N, int64_t K, const void *A,
+                                         int64_t lda, const float *a_scale, const void *B,
+                                         int64_t ldb, int64_t b_group_stride, const float *b_scale,
+                                         int64_t b_scale_group_stride, void *Y, int64_t ldy,
+                                         void *stream, const qlin_config *cfg)
+{
+    if (groups < 0)
+        return QLIN_ERR_BAD_SHAPE;
+    if (groups == 0)
+        return QLIN_OK;
+    Problem pb = make_problem(FMT_E4M3, SC_BLOCK, max_rows, N, K, A, lda, a_scale, B, ldb, b_scale,
+                              Y, ldy, nullptr, 0, stream);
+    pb.groups = groups;
+    pb.group_off = group_offsets;
+    pb.b_gstride = b_group_stride;
+    pb.sb_gstride = b_scale_group_stride;
+    return run(pb, cfg);
 }
 
 qlin_status qlin_int8_accumulate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,

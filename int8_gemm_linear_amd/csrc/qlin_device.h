@@ -266,4 +266,27 @@ __device__ inline typename AccT<FMT>::scalar *part_ptr(const KArgs &p, int split
     return reinterpret_cast<S *>(p.part) + ((int64_t)split * p.M + t) * p.N + n;
 }
 
+// Grouped GEMM: narrows the arguments to the workgroup's group (grid.z).
+// p.M holds the bound on rows per group; the group's own row count caps it.
+// Returns false when the group is empty.  Called first thing in a kernel,
+// before any barrier, so a workgroup with nothing to do simply returns.
+template <int SCAL>
+__device__ inline bool enter_group(KArgs &p)
+{
+    const int g = blockIdx.z;
+    const int m_beg = p.group_off[g];
+    p.M = min(p.group_off[g + 1] - m_beg, p.M);
+    if (p.M <= 0)
+        return false;
+    p.A += (int64_t)m_beg * p.lda;
+    p.sA += SCAL == SC_BLOCK ? (int64_t)m_beg * p.G : (int64_t)m_beg;
+    p.Y += (int64_t)m_beg * p.ldy;
+    p.B += (int64_t)g * p.b_gstride;
+    p.sB += (int64_t)g * p.sb_gstride;
+    return true;
+}
+
+// Split index of the workgroup: grid.z, unless grid.z is the group.
+__device__ inline int split_index(const KArgs &p) { return p.group_off ? 0 : (int)blockIdx.z; }
+
 }  // namespace qlin

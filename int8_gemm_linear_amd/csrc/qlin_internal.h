@@ -33,6 +33,13 @@ struct KArgs {
     int split_k;
     int steps_per_split; // 128-byte K steps per split
     int reduce;          // qlin_reduce
+    // Grouped GEMM (mixture of experts): grid.z is the group; group g owns
+    // rows group_off[g] .. group_off[g+1]-1 of A, sA and Y (at most M of
+    // them) and the weights B + g * b_gstride bytes, sB + g * sb_gstride.
+    // NULL for an ordinary call.
+    const int32_t *group_off;
+    int64_t b_gstride;
+    int64_t sb_gstride;
 };
 
 // Host-side description of a problem.
@@ -53,6 +60,12 @@ struct Problem {
     void *ws;
     size_t ws_bytes;
     hipStream_t stream;
+    // grouped GEMM: groups > 0 and the device row offsets of the groups;
+    // M is then the bound on rows per group
+    int64_t groups;
+    const int32_t *group_off;
+    int64_t b_gstride;   // bytes
+    int64_t sb_gstride;  // floats
 };
 
 typedef hipError_t (*LaunchFn)(const KArgs &a, dim3 grid, hipStream_t s);

@@ -46,8 +46,11 @@ struct StreamFrag {
 
 template <int FMT, int SCAL, bool SWAP, int TB, int RB, int WN, int WK, int U>
 __global__ void __launch_bounds__(64 * WN * WK)
-k_stream(KArgs p)
+k_stream(KArgs p_)
 {
+    KArgs p = p_;
+    if (p.group_off && !enter_group<SCAL>(p))
+        return;
     typedef typename AccT<FMT>::v4 A4;
     typedef typename AccT<FMT>::scalar AS;
     typedef StreamFrag<FMT, SCAL, TB, RB, U> Frag;
@@ -64,7 +67,9 @@ k_stream(KArgs p)
 
     const int nw0 = blockIdx.x * TILE_N + wn * ROWS_W;
     const int m0 = blockIdx.y * TILE_M;
-    const int split = blockIdx.z;
+    const int split = split_index(p);
+    if (m0 >= p.M)
+        return;                 // a group with fewer rows than the grid covers
 
     const int KS = (p.K + 127) >> 7;
     const int s_beg = min(KS, split * p.steps_per_split);

@@ -57,7 +57,7 @@ __device__ inline void wait_vm()
 
 template <int FMT, bool SWAP, int TMS, int TRW, int NW, int S, int CHK>
 __global__ void __launch_bounds__(64 * NW)
-k_stream_lds(KArgs p)
+k_stream_lds(KArgs p_)
 {
     typedef typename AccT<FMT>::v4 A4;
     typedef typename AccT<FMT>::scalar AS;
@@ -83,9 +83,14 @@ k_stream_lds(KArgs p)
     const int r16 = lane & 15;
     const int g = lane >> 4;
 
+    KArgs p = p_;
+    if (p.group_off && !enter_group<SC_TC>(p))
+        return;
     const int n0 = blockIdx.x * TR;
     const int m0 = blockIdx.y * TMS;
-    const int split = blockIdx.z;
+    const int split = split_index(p);
+    if (m0 >= p.M)
+        return;                 // a group with fewer rows than the grid covers
 
     // K range of this split, in 256-byte units.
     const int KP = p.K >> 8;

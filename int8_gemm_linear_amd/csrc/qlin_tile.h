@@ -120,6 +120,15 @@ __device__ inline void tile_origin(const KArgs &p, int &m0, int &n0)
     n0 = (in_grp / gsize) * BN;
 }
 
+// A grouped call sizes grid.x for the largest group: workgroups past the
+// tiles of their own (smaller) group have nothing to do.
+template <int BM, int BN>
+__device__ inline bool tile_in_group(const KArgs &p)
+{
+    const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    return (int)blockIdx.x < tiles;
+}
+
 // Epilogue of a tile: the wave's FM x FN accumulator blocks of 32x32 are
 // either scaled, rounded and stored (no split), or written as split-K
 // partials; with the last-arriver reduction the last workgroup of the tile
@@ -137,7 +146,7 @@ __device__ inline void tile_finish(const KArgs &p,
     constexpr int FN = WTN / 32;
     const int fr = lane & 31;
     const int fh = lane >> 5;
-    const int split = blockIdx.z;
+    const int split = split_index(p);
 
     // Output positions of acc[fm][fn][v] for this lane:
     //   SWAP:     t = tok0 + fr,  n = wgt0 + 8*(v/4) + 4*fh + v%4  (4 consecutive n per v/4)
@@ -381,7 +390,7 @@ __device__ inline void tile_finish(const KArgs &p,
 
 template <int FMT, int SCAL, bool SWAP, int BM, int BN, int WM, int WN, int S>
 __global__ void __launch_bounds__(64 * WM * WN)
-k_tile(KArgs p)
+k_tile(KArgs p_)
 {
     typedef typename AccT<FMT>::v16 A16;
     typedef typename AccT<FMT>::scalar AS;
@@ -399,6 +408,10 @@ k_tile(KArgs p)
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[S * STAGE];
 
+    KArgs p = p_;
+    if (p.group_off && !(enter_group<SCAL>(p) && tile_in_group<BM, BN>(p)))
+        return;
+
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave / WN;
@@ -409,7 +422,7 @@ k_tile(KArgs p)
 
     // ---- K range of this split (128-byte steps)
     const int KS = p.K >> 7;
-    const int split = blockIdx.z;
+    const int split = split_index(p);
     const int s_beg = min(KS, split * p.steps_per_split);
     const int s_end = min(KS, s_beg + p.steps_per_split);
 

@@ -97,7 +97,7 @@ __device__ inline v16f mma_half<FMT_E4M3>(const v4i (&x)[2], const v4i (&y)[2], 
 
 template <int FMT, bool SWAP, int BM, int BN, int WM, int WN, int S>
 __global__ void __launch_bounds__(64 * WM * WN)
-k_tile_h(KArgs p)
+k_tile_h(KArgs p_)
 {
     typedef typename AccT<FMT>::v16 A16;
     constexpr int NW = WM * WN;
@@ -128,12 +128,16 @@ k_tile_h(KArgs p)
     const int fr = lane & 31;
     const int fh = lane >> 5;
 
+    KArgs p = p_;
+    if (p.group_off && !(enter_group<SC_TC>(p) && tile_in_group<BM, BN>(p)))
+        return;
+
     int m0, n0;
     tile_origin<BM, BN>(p, m0, n0);
 
     // K range of this split, in 64-byte half-steps.
     const int KS = p.K >> 7;
-    const int split = blockIdx.z;
+    const int split = split_index(p);
     const int s_beg = min(KS, split * p.steps_per_split);
     const int s_end = min(KS, s_beg + p.steps_per_split);
     const int h_beg = 2 * s_beg;
@@ -263,11 +267,9 @@ hipError_t launch_tile_h(const KArgs &a, dim3 grid, hipStream_t s)
      &launch_tile_h<FMT, (SW) != 0, BM, BN, WM, WN, S>}
 
 // (BM, BN, WM, WN, S); LDS = S * (BM + BN) * 64 B.
+// (The 8-wave 256x256 forms, with two fragment sets and 128 accumulators per
+// wave, do not fit 256 registers and spill; they are not built.)
 #define QLIN_TILE_H_SHAPES(X, FMT, BIT, SW) \
-    X(FMT, BIT, SW, 256, 256, 2, 4, 5),     \
-    X(FMT, BIT, SW, 256, 256, 4, 2, 5),     \
-    X(FMT, BIT, SW, 256, 256, 2, 4, 4),     \
-    X(FMT, BIT, SW, 256, 256, 4, 2, 4),     \
     X(FMT, BIT, SW, 256, 128, 4, 2, 6),     \
     X(FMT, BIT, SW, 256, 256, 2, 2, 4),     \
     X(FMT, BIT, SW, 256, 128, 2, 2, 6),     \

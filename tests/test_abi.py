@@ -286,3 +286,37 @@ def test_fused_producer_validation_errors():
     assert frms(eps=0.0) == ST["arg"]
     assert frms(eps=float("inf")) == ST["arg"]
     assert frms(eps=float("nan")) == ST["arg"]
+
+
+def grp(dt=q.E4M3, G=4, off=S4, max_rows=8, N=256, K=1024, A=A16, lda=None, sa=S4, B=B16,
+        ldb=None, bstride=None, sb=S4, sbstride=256, Y=B16, ldy=None, block=False, cfg=None):
+    lib = q.lib()
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    bstride = N * ldb if bstride is None else bstride
+    ldy = N if ldy is None else ldy
+    if block:
+        return lib.qlin_grouped_block_scaled_mm(G, off, max_rows, N, K, A, lda, sa, B, ldb, bstride,
+                                                sb, sbstride, Y, ldy, None, cfg)
+    return lib.qlin_grouped_scaled_mm(dt, G, off, max_rows, N, K, A, lda, sa, B, ldb, bstride, sb,
+                                      sbstride, Y, ldy, None, cfg)
+
+
+def test_grouped_validation_errors():
+    # argument checks return before any launch (no GPU needed)
+    assert grp(dt=9) == ST["arg"]
+    assert grp(G=-1) == ST["shape"]
+    assert grp(G=0, off=None) == ST["ok"]                  # no groups: no-op
+    assert grp(max_rows=0, off=None) == ST["ok"]           # no rows: no-op
+    assert grp(G=65536) == ST["shape"]
+    assert grp(K=24) == ST["shape"]
+    assert grp(N=200, block=True) == ST["shape"]           # block needs N % 128
+    assert grp(off=None) == ST["null"]
+    assert grp(off=S4 + 2) == ST["align"]
+    assert grp(bstride=8) == ST["stride"]                  # group stride % 16
+    assert grp(bstride=-16) == ST["stride"]
+    assert grp(sbstride=-1) == ST["stride"]
+    assert grp(lda=1000) == ST["stride"]
+    assert grp(A=A16 + 8) == ST["align"]
+    c = q.select_config("fp8", 8, 256, 1024).replace(split_k=2, reduce=0)
+    assert grp(cfg=ctypes.byref(c._c())) == ST["cfg"]      # grid.z is the group
