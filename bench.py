@@ -320,6 +320,93 @@ def producer_points(reps: int = 8, target_bytes: int = 1 << 30):
             "copies (~1 GiB between reuses), hipEvents", "points": out}
 
 
+# Mixture-of-experts layers of a 30B-class model with 3B active parameters
+# (hidden 2048, 128 experts, 8 per token, expert width 768): gate_up
+# (K=2048, N=1536) and down (K=768, N=2048), FP8_Dynamic, at decode batches
+# of 1 and 32 tokens and a 512-token prefill.  Routing: each token picks 8
+# distinct experts uniformly (seeded); tokens are sorted by expert.
+MOE_LAYERS = [("gate_up", 2048, 1536), ("down", 768, 2048)]
+MOE_EXPERTS, MOE_TOPK = 128, 8
+MOE_BATCHES = [1, 32, 512]
+
+
+def moe_points(reps: int = 8, target_bytes: int = 1 << 30):
+    """One grouped launch per MoE layer call (device offset table), timed
+    from a graph over rotating weight copies; beside it the same work as one
+    scaled_mm launch per active expert (captured likewise) for comparison.
+    Algorithmic bytes: each active expert's weights and scales once, its
+    token rows and outputs once."""
+    import torch
+    import int8_gemm_linear_amd as q
+    import synth
+    dev = torch.device("cuda:0")
+    out = []
+    for name, K, N in MOE_LAYERS:
+        E = MOE_EXPERTS
+        w = torch.from_numpy(np.ascontiguousarray(
+            synth.rng(81, K, N).integers(0, 0x7E, (E, N, K), dtype=np.uint8) |
+            (synth.rng(82, K, N).integers(0, 2, (E, N, K), dtype=np.uint8) << 7))).to(dev)
+        w = w.view(torch.float8_e4m3fn)
+        sb = torch.full((E, N), 1e-3, dtype=torch.float32, device=dev)
+        copies = max(2, -(-target_bytes // (E * N * K)))
+        ws = [w] + [w.clone() for _ in range(copies - 1)]
+        for B in MOE_BATCHES:
+            g = synth.rng(83, B, K)
+            picks = np.stack([g.choice(E, MOE_TOPK, replace=False) for _ in range(B)])
+            counts = np.bincount(picks.ravel(), minlength=E)
+            rows = int(counts.sum())
+            off = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
+            a = torch.from_numpy(synth.rng(84, B, K).integers(0, 0x7E, (rows, K), dtype=np.uint8)).to(dev)
+            a = a.view(torch.float8_e4m3fn)
+            sa = torch.full((rows,), 1e-2, dtype=torch.float32, device=dev)
+            y = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
+            max_rows = int(counts.max())
+            n = max(reps, copies)
+
+            def grouped(i):
+                q.grouped_scaled_mm(a, sa, ws[i % copies], sb, off, max_rows, out=y)
+
+            act = [e for e in range(E) if counts[e] > 0]
+            starts = np.concatenate([[0], np.cumsum(counts)])
+
+            def loop(i):
+                wi = ws[i % copies]
+                for e in act:
+                    lo, hi = int(starts[e]), int(starts[e + 1])
+                    q.scaled_mm(a[lo:hi], sa[lo:hi], wi[e], sb[e], out=y[lo:hi])
+
+            def timed(fn, calls):
+                fn(0)
+                torch.cuda.synchronize()
+                gr = capture(lambda: [fn(i) for i in range(calls)])
+                gr.replay()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                gr.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                del gr
+                return e0.elapsed_time(e1) * 1e3 / calls
+
+            us = timed(grouped, n)
+            loop_us = timed(loop, min(n, 4))
+            nb = len(act) * (N * K + 4 * N) + rows * (K + 2 * N + 4)
+            cfg = q.select_grouped_config("fp8", max_rows, N, K)
+            out.append({"layer": name, "K": K, "N": N, "batch": B, "experts_active": len(act),
+                        "rows": rows, "max_rows": max_rows, "us": round(us, 2), "alg_bytes": nb,
+                        "tbs": round(nb / us / 1e6, 3), "frac": round(nb / us / 1e6 / 8.0, 4),
+                        "tflops": round(2.0 * rows * N * K / us / 1e6, 1),
+                        "per_expert_launches_us": round(loop_us, 2),
+                        "cfg": f"k{cfg.kernel} v{cfg.variant} {cfg.tile_m}x{cfg.tile_n}x{cfg.tile_k} "
+                               f"w{cfg.waves_n}x{cfg.waves_k} s{cfg.stages} split1"})
+        del ws, w
+        torch.cuda.empty_cache()
+    return {"unit": "TB/s", "peak_tbs": 8.0, "model": "128 experts, top-8, hidden 2048, expert width 768",
+            "timing": "HIP-graph replay, rotating weight copies (>= 1 GiB), hipEvents", "points": out}
+
+
 def cpu_model() -> str:
     try:
         for ln in open("/proc/cpuinfo"):
@@ -373,6 +460,7 @@ def main():
     ap.add_argument("--per-point", action="store_true", help="print per-point timings to stderr")
     ap.add_argument("--no-dispatch", action="store_true", help="skip the host dispatch-cost run")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M >= 512 per-point timings")
+    ap.add_argument("--no-moe", action="store_true", help="skip the grouped (MoE) GEMM timings")
     ap.add_argument("--no-producers", action="store_true",
                     help="skip the activation-producer timings (quantizers, fused norm / SiLU)")
     args = ap.parse_args()
@@ -452,6 +540,9 @@ def main():
     producers = None
     if not args.no_producers and args.workload != "prefill":
         producers = producer_points()
+    moe = None
+    if not args.no_moe and args.workload != "prefill":
+        moe = moe_points()
 
     flops_tops = wl.flops_per_step / (ms_step * 1e-3) / 1e12
     out = {
@@ -485,6 +576,7 @@ def main():
         "dispatch": dispatch,
         "prefill_mfma": prefill,
         "producers": producers,
+        "moe_grouped": moe,
         "parity_vs_oracle": parity_ok,
     }
     print(json.dumps(out), flush=True)

@@ -189,8 +189,8 @@ qlin_status qlin_block_scaled_mm_cfg(int64_t M, int64_t N, int64_t K,
  * must hold group_offsets[groups] rows.  Per-group layouts and scales as in
  * qlin_scaled_mm (token/channel) or qlin_block_scaled_mm (b_scale of a
  * group [N/128][K/128]).  b_group_stride % 16 == 0, both strides >= 0.
- * groups <= 65535 (0 is a no-op).  The config (NULL: the table's choice
- * for (N, K) at M = max_rows) runs with split_k = 1: the groups fill the
+ * groups <= 65535 (0 is a no-op).  The config (NULL: the grouped choice,
+ * qlin_select_grouped_config) runs with split_k = 1: the groups fill the
  * machine, grid.z carries the group, and no workspace is used; a config
  * with split_k > 1 is rejected.  Empty groups cost one early-exiting
  * workgroup per tile.  Asynchronous on `stream`; allocates nothing; errors
@@ -201,6 +201,10 @@ qlin_status qlin_grouped_scaled_mm(qlin_dtype dt, int64_t groups, const int32_t 
                                    int64_t b_group_stride, const float *b_scale,
                                    int64_t b_scale_group_stride, void *Y, int64_t ldy, void *stream,
                                    const qlin_config *cfg);
+/* The config a grouped call uses when given none: split_k = 1 and a kernel
+ * chosen by the bound on rows per group (measured on 128-expert layers). */
+qlin_status qlin_select_grouped_config(qlin_scaling sc, qlin_dtype dt, int64_t max_rows,
+                                       int64_t N, int64_t K, qlin_config *out);
 qlin_status qlin_grouped_block_scaled_mm(int64_t groups, const int32_t *group_offsets,
                                          int64_t max_rows, int64_t N, int64_t K, const void *A,
                                          int64_t lda, const float *a_scale, const void *B,

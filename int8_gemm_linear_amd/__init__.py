@@ -142,6 +142,8 @@ def _lib():
     lib.qlin_grouped_block_scaled_mm.argtypes = [I64, P, I64, I64, I64, P, I64, P, P, I64, I64, P,
                                                  I64, P, I64, P, CP]
     lib.qlin_grouped_block_scaled_mm.restype = I
+    lib.qlin_select_grouped_config.argtypes = [I, I, I64, I64, I64, CP]
+    lib.qlin_select_grouped_config.restype = I
     lib.qlin_rms_norm_dynamic_per_token_quant.argtypes = [I, I64, I64, P, I64, P, I64, P, F, P, I64, P, P]
     lib.qlin_rms_norm_dynamic_per_token_quant.restype = I
     lib.qlin_rms_norm_per_block_quant.argtypes = [I64, I64, P, I64, P, I64, P, F, P, I64, P, P]
@@ -519,6 +521,15 @@ def select_config(fmt: str, M: int, N: int, K: int) -> Config:
     sc, dt = FORMATS[fmt]
     c = _Cfg()
     _call(_lib().qlin_select_config, [sc, dt, M, N, K, ctypes.byref(c)], "qlin_select_config")
+    return Config._from_c(c)
+
+
+def select_grouped_config(fmt: str, max_rows: int, N: int, K: int) -> Config:
+    """The config a grouped call uses by default (split_k = 1)."""
+    sc, dt = FORMATS[fmt]
+    c = _Cfg()
+    _call(_lib().qlin_select_grouped_config, [sc, dt, max_rows, N, K, ctypes.byref(c)],
+          "qlin_select_grouped_config")
     return Config._from_c(c)
 
 

@@ -248,6 +248,15 @@ qlin_config default_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
 qlin_status check_config(int fmt, int scal, int64_t M, int64_t N, int64_t K,
                          const qlin_config &c, const Instance **inst);
 
+// Grouped (mixture-of-experts) calls: split_k = 1 (grid.z is the expert)
+// and a kernel chosen by the bound on rows per expert, from a sweep of every
+// instance over 128-expert layers (K, N) = (2048, 1536) and (768, 2048) at
+// 1-52 rows per expert: the LDS-ring stream kernel with 8-token tiles up to
+// 3 rows, the register stream kernel with 16x64 tiles up to 16, a 64x128
+// tile up to 64 and a 128x128 tile beyond.  A choice this build lacks for
+// the format falls back to the table's config with split_k = 1.
+qlin_config grouped_config(int fmt, int scal, int64_t M, int64_t N, int64_t K);
+
 qlin_config select_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
 {
     ensure_table();
@@ -271,6 +280,33 @@ qlin_config select_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
     if (best && check_config(fmt, scal, M, N, K, best->cfg, nullptr) == QLIN_OK)
         return best->cfg;
     return default_config(fmt, scal, M, N, K);
+}
+
+qlin_config grouped_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
+{
+    auto make = [](int kernel, int tm, int tn, int tk, int wn, int wk, int st) {
+        qlin_config c;
+        std::memset(&c, 0, sizeof c);
+        c.kernel = kernel;
+        c.variant = QLIN_SWAP_AB;
+        c.tile_m = tm, c.tile_n = tn, c.tile_k = tk;
+        c.waves_n = wn, c.waves_k = wk, c.stages = st;
+        c.split_k = 1;
+        c.reduce = QLIN_REDUCE_LAST_ARRIVER;
+        return c;
+    };
+    const qlin_config pick =
+        M <= 3    ? make(QLIN_KERNEL_STREAM_LDS, 8, 16, 512, 1, 4, 4)
+        : M <= 16 ? make(QLIN_KERNEL_STREAM, 16, 64, 128, 1, 4, 2)
+        : M <= 64 ? (scal == SC_TC ? make(QLIN_KERNEL_TILE, 64, 128, 128, 1, 4, 4)
+                                   : make(QLIN_KERNEL_TILE, 64, 128, 128, 1, 4, 2))
+                  : make(QLIN_KERNEL_TILE, 128, 128, 128, 2, 2, 2);
+    if (check_config(fmt, scal, M, N, K, pick, nullptr) == QLIN_OK)
+        return pick;
+    qlin_config c = select_config(fmt, scal, M, N, K);
+    c.split_k = 1;
+    c.reduce = QLIN_REDUCE_LAST_ARRIVER;
+    return c;
 }
 
 qlin_status check_config(int fmt, int scal, int64_t M, int64_t N, int64_t K,
@@ -363,11 +399,9 @@ qlin_status run(const Problem &pb, const qlin_config *cfg_in)
         if (cfg_in && cfg_in->split_k != 1)
             return QLIN_ERR_BAD_CONFIG;   // grid.z carries the group
     }
-    qlin_config cfg = cfg_in ? *cfg_in : select_config(pb.fmt, pb.scal, pb.M, pb.N, pb.K);
-    if (grouped && !cfg_in) {
-        cfg.split_k = 1;                  // the groups fill the machine instead
-        cfg.reduce = QLIN_REDUCE_LAST_ARRIVER;
-    }
+    const qlin_config cfg = cfg_in    ? *cfg_in
+                            : grouped ? grouped_config(pb.fmt, pb.scal, pb.M, pb.N, pb.K)
+                                      : select_config(pb.fmt, pb.scal, pb.M, pb.N, pb.K);
     const Instance *inst = nullptr;
     st = check_config(pb.fmt, pb.scal, pb.M, pb.N, pb.K, cfg, &inst);
     if (st != QLIN_OK)
@@ -566,6 +600,20 @@ qlin_status qlin_select_config(qlin_scaling sc, qlin_dtype dt, int64_t M, int64_
     if (M < 0 || N < 0 || K <= 0)
         return QLIN_ERR_BAD_SHAPE;
     *out = select_config(fmt, sc == QLIN_BLOCK128 ? SC_BLOCK : SC_TC, M, N, K);
+    return QLIN_OK;
+}
+
+qlin_status qlin_select_grouped_config(qlin_scaling sc, qlin_dtype dt, int64_t max_rows, int64_t N,
+                                       int64_t K, qlin_config *out)
+{
+    const int fmt = fmt_of(dt);
+    if (fmt < 0 || (sc != QLIN_TOKEN_CHANNEL && sc != QLIN_BLOCK128) ||
+        (sc == QLIN_BLOCK128 && fmt != FMT_E4M3))
+        return QLIN_ERR_BAD_ARGUMENT;
+    if (!out)
+        return QLIN_ERR_NULL_POINTER;
+    ensure_table();
+    *out = grouped_config(fmt, sc == QLIN_BLOCK128 ? SC_BLOCK : SC_TC, max_rows, N, K);
     return QLIN_OK;
 }
 

@@ -320,3 +320,12 @@ def test_grouped_validation_errors():
     assert grp(A=A16 + 8) == ST["align"]
     c = q.select_config("fp8", 8, 256, 1024).replace(split_k=2, reduce=0)
     assert grp(cfg=ctypes.byref(c._c())) == ST["cfg"]      # grid.z is the group
+
+
+def test_grouped_default_config_is_valid_and_unsplit():
+    for fmt in ("fp8", "int8", "block_fp8"):
+        for mr in (1, 3, 4, 16, 17, 64, 65, 300):
+            for (N, K) in ((1536, 2048), (2048, 768), (256, 1024)):
+                c = q.select_grouped_config(fmt, mr, N, K)
+                assert c.split_k == 1, (fmt, mr, c)
+                assert q.check_config(fmt, mr, N, K, c) == 0, (fmt, mr, N, K, c)
