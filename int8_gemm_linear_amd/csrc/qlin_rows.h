@@ -6,9 +6,10 @@
 // +4 for a residual read and written back) and 1 byte out.  What keeps them
 // at the bandwidth is latency hiding, so a row is as few waves as fit it in
 // registers (W = 1 for rows up to 4096 values, 2 up to 8192, ... 8 up to
-// 32768): every lane issues all its 16-byte loads (kReg pieces) before it
-// uses any, a single-wave row reduces with shuffles alone, and small
-// workgroups let many rows be in flight per CU.  Lane t of the row owns the
+// 32768) when there are rows enough to fill the machine, more (up to 8)
+// when there are not: every lane issues all its 16-byte loads (kReg
+// pieces) before it uses any, a single-wave row reduces with shuffles
+// alone, and small workgroups let many rows be in flight per CU.  Lane t of the row owns the
 // pieces t, t + 64W, ...; pieces beyond the register window (rows longer
 // than 32768) are produced again from the L2-resident input in the
 // quantizer's second pass.  Per-group scaling needs no row reduction: the
@@ -61,13 +62,23 @@ __device__ inline double dlo(uint32_t w) { return (double)bf16_lo(w); }
 __device__ inline double dhi(uint32_t w) { return (double)bf16_hi(w); }
 __device__ inline uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
 
-// h = bf16(x + r) for 8 values.
+// h = bf16(x + r) for 8 values.  The fp32 sum of two bf16 values is exact
+// unless their exponents differ by more than 16, and then the sum lies
+// within 2^-16 of the larger value, far from any bf16 rounding boundary
+// around it: rounding the fp32 sum to bf16 (nearest even) gives the bf16
+// rounding of the exact sum.
+__device__ inline uint32_t bf16_rne(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 __device__ inline u32x4 add_round8(u32x4 x, u32x4 r)
 {
     u32x4 h;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        h[j] = pack2(bf16_of_double(dlo(x[j]) + dlo(r[j])), bf16_of_double(dhi(x[j]) + dhi(r[j])));
+        h[j] = pack2(bf16_rne(bf16_lo(x[j]) + bf16_lo(r[j])), bf16_rne(bf16_hi(x[j]) + bf16_hi(r[j])));
     return h;
 }
 
@@ -96,15 +107,17 @@ __device__ inline u32x4 norm8(u32x4 h, u32x4 w, double inv)
 // Fast path in fp32 for |g| <= 64: p = -g log2(e) carried as p_hi + p_lo
 // (p_lo from an fma: the argument is exact to ~2^-48), e^-g = 2^p_hi *
 // (1 + p_lo ln 2) with the hardware exp2 (~1 ulp), then 1 + t, the hardware
-// reciprocal (~1 ulp) and two products: with a few ulp allowed per hardware
-// step, y32 is within 2^-20 (16 ulp) of the real value.  When every
-// intermediate is a normal fp32 number and y32's low 16 bits are more than
-// 64 ulp from the bf16 tie pattern 0x8000, no bf16 rounding boundary lies
-// between y32 and the real value, so rounding y32 gives the same bf16.  The
-// other values (about 0.2%, and |g| > 64 where e^-g leaves fp32) are
-// computed in double (library exp, correctly rounded division) and rounded
-// once.
-// Out of line: rare, and inlined at every value it would multiply the code size.
+// reciprocal (~1 ulp) and two products.  Measured on the MI355X against the
+// double evaluation over every bf16 gate in [-64, 64] times 256 bf16 ups
+// (6.75 million pairs): y32 is within 3.4 fp32 ulp of the real value.  When
+// every intermediate is a normal fp32 number and y32's low 16 bits are more
+// than 24 ulp (7x that) from the bf16 tie pattern 0x8000, no bf16 rounding
+// boundary lies between y32 and the real value, so rounding y32 gives the
+// same bf16.  The other values (about 0.07%, and |g| > 64 where e^-g leaves
+// fp32) are computed in double (library exp, correctly rounded division)
+// and rounded once.
+// Out of line: rare, and inlined it would raise the register count of every
+// SiLU kernel (and multiply the code size).
 __device__ __attribute__((noinline)) uint32_t silu_exact(float g, float u)
 {
     const double gd = g;
@@ -137,7 +150,7 @@ __device__ inline u32x4 silu8(u32x4 gw, u32x4 uw)
         const float as = fabsf(sv), ay = fabsf(y);
         const uint32_t bits = __float_as_uint(y);
         const bool ok = fabsf(g[j]) <= 64.0f && as >= 0x1p-100f && ay >= 0x1p-100f &&
-                        ay <= 0x1p+100f && ((bits & 0xFFFFu) - 0x7FC0u) >= 128u;
+                        ay <= 0x1p+100f && ((bits & 0xFFFFu) - 0x7FE8u) >= 48u;
         need |= ok ? 0u : 1u << j;
         b[j] = (bits + 0x7FFFu + ((bits >> 16) & 1u)) >> 16;
     }
@@ -322,12 +335,17 @@ k_rows(RowArgs a)
     }
 }
 
-// Waves per row: the fewest that hold the row's pieces in registers.
-inline int waves_for(int64_t K)
+// Waves per row: the fewest that hold the row's pieces in registers, and
+// more while the grid has fewer than 2048 waves: with few rows (decode) the
+// per-lane work of a one-wave row is a long serial chain, so the row is
+// spread over up to 8 waves instead.
+inline int waves_for(int64_t M, int64_t K)
 {
     const int64_t P = K >> 3;
     int w = 1;
     while (w < kMaxW && (int64_t)64 * w * kReg < P)
+        w *= 2;
+    while (w < kMaxW && M * w < 2048 && (int64_t)64 * w < P)
         w *= 2;
     return w;
 }
@@ -336,7 +354,12 @@ template <int OP, int QM, bool RES>
 hipError_t launch_rows(const RowArgs &a, int64_t M, hipStream_t s)
 {
     const dim3 grid((unsigned)M);
-    switch (waves_for(a.K)) {
+    // SiLU-and-mul rows take at most 4 waves: its kernels need ~125
+    // registers, so an 8-wave workgroup would leave room for only one per
+    // CU; longer rows recompute the pieces past the register window
+    // (measured faster: 113 vs 134 us at 2048 x 25600).
+    const int w = waves_for(M, a.K);
+    switch (OP == OP_SILU && w > 4 ? 4 : w) {
     case 1: hipLaunchKernelGGL((k_rows<OP, QM, 1, RES>), grid, dim3(64), 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_rows<OP, QM, 2, RES>), grid, dim3(128), 0, s, a); break;
     case 4: hipLaunchKernelGGL((k_rows<OP, QM, 4, RES>), grid, dim3(256), 0, s, a); break;

@@ -56,8 +56,9 @@ def _is_qlin(name: str) -> bool:
     return "qlin::" in name
 
 
-def kernel_durations(folder: str) -> dict[str, list[float]]:
-    """{kernel name: [duration ns, ...]} from a kernel-trace folder."""
+def kernel_durations(folder: str, by_grid: bool = False) -> dict[str, list[float]]:
+    """{kernel name (with " grid=x,y,z" when by_grid): [duration ns, ...]}
+    from a kernel-trace folder."""
     out: dict[str, list[float]] = collections.OrderedDict()
     csvs = glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True)
     if csvs:
@@ -65,25 +66,41 @@ def kernel_durations(folder: str) -> dict[str, list[float]]:
             with open(p, newline="") as f:
                 for r in csv.DictReader(f):
                     d = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
-                    out.setdefault(r["Kernel_Name"], []).append(d)
+                    k = r["Kernel_Name"]
+                    if by_grid:
+                        k += " grid=%s,%s,%s" % (r.get("Grid_Size_X", "?"), r.get("Grid_Size_Y", "?"),
+                                                 r.get("Grid_Size_Z", "?"))
+                    out.setdefault(k, []).append(d)
         return out
     dbs = glob.glob(os.path.join(folder, "**", "*.db"), recursive=True)
     if not dbs:
         raise SystemExit(f"no kernel trace under {folder}")
     for p in dbs:
         db = sqlite3.connect(p)
-        for name, d in db.execute("select name, duration from kernels"):
-            out.setdefault(name, []).append(float(d))
+        if by_grid:
+            rows = db.execute("select name, duration, grid_size_x, grid_size_y, grid_size_z "
+                              "from kernels")
+            for name, d, gx, gy, gz in rows:
+                out.setdefault(f"{name} grid={gx},{gy},{gz}", []).append(float(d))
+        else:
+            for name, d in db.execute("select name, duration from kernels"):
+                out.setdefault(name, []).append(float(d))
     return out
 
 
-def trace_summary(folder: str) -> str:
-    agg = kernel_durations(folder)
+def trace_summary(folder: str, by_grid: bool = False, match: str | None = None,
+                  grid_z: int | None = None) -> str:
+    agg = kernel_durations(folder, by_grid or grid_z is not None)
+    if match:
+        agg = collections.OrderedDict((k, v) for k, v in agg.items() if match in k)
+    if grid_z is not None:
+        agg = collections.OrderedDict((k, v) for k, v in agg.items()
+                                      if k.rsplit(",", 1)[-1] == str(grid_z))
     lines = [f"{'calls':>6} {'avg_us':>9} {'min_us':>8} {'max_us':>8} {'total_ms':>9}  kernel"]
     for name, ds in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         d = np.array(ds) / 1e3
         lines.append(f"{len(d):6d} {d.mean():9.3f} {d.min():8.3f} {d.max():8.3f} "
-                     f"{d.sum() / 1e3:9.3f}  {name[:110]}")
+                     f"{d.sum() / 1e3:9.3f}  {name[:140]}")
     gemm = [k for k in agg if _is_gemm(k)]
     red = [k for k in agg if "qlin::k_reduce" in k]
     if gemm:
@@ -187,6 +204,10 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     t = sub.add_parser("trace")
     t.add_argument("folder")
+    t.add_argument("--by-grid", action="store_true", help="one line per (kernel, grid)")
+    t.add_argument("--match", default=None, help="only kernels whose line contains this text")
+    t.add_argument("--grid-z", type=int, default=None,
+                   help="only launches with this grid.z (e.g. the expert count of grouped calls)")
     m = sub.add_parser("mfma")
     m.add_argument("folder")
     c = sub.add_parser("traffic")
@@ -199,7 +220,7 @@ def main(argv=None):
     c.add_argument("--per-launch", action="store_true", help="also print per (kernel, grid) means")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
-        print(trace_summary(a.folder))
+        print(trace_summary(a.folder, a.by_grid, a.match, a.grid_z))
         return
     if a.cmd == "mfma":
         print(mfma_summary(a.folder))
