@@ -559,7 +559,37 @@ k_tile(KArgs p_)
                                            : mma32_piece<FMT>(af, bf[fn], j, acc[fm][fn]);
             }
         };
-        if constexpr (SCAL == SC_BLOCK) {
+        if constexpr (SCAL == SC_BLOCK && NW >= 8) {
+            // Block scaling with 8 waves (256 registers per lane): pipelined
+            // one 32x32 block deep, the group product of block k+1 on the
+            // matrix cores while the VALU promotes block k, with two product
+            // tiles and one A-fragment set live (the A-block-deep pipeline
+            // below would hold 2 x FN product tiles and spill); the other
+            // wave of the SIMD covers the LDS read of the next A block.
+            constexpr int NB = FM * FN;
+            A16 pz[2];
+            v4i af[4];
+            const A16 zero = {};
+            load_a(af, 0);
+            pz[0] = SWAP ? mma32<FMT>(bf[0], af, zero) : mma32<FMT>(af, bf[0], zero);
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const int fm = k / FN;
+                const int fn = k % FN;
+                if (k + 1 < NB) {
+                    const int fm1 = (k + 1) / FN;
+                    const int fn1 = (k + 1) % FN;
+                    if (fn1 == 0)
+                        load_a(af, fm1);
+                    pz[(k + 1) & 1] = SWAP ? mma32<FMT>(bf[fn1], af, zero)
+                                           : mma32<FMT>(af, bf[fn1], zero);
+                }
+                const float scale = sa[fm] * sb[fn];
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc[fm][fn][v] = __builtin_fmaf((float)pz[k & 1][v], scale, (float)acc[fm][fn][v]);
+            }
+        } else if constexpr (SCAL == SC_BLOCK) {
             // Block scaling, software-pipelined across the 32-row A blocks:
             // the group products of block fm+1 go to the matrix cores while
             // the VALU promotes block fm's (acc += p * sA * sB), so the two
