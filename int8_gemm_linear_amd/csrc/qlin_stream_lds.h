@@ -387,6 +387,8 @@ hipError_t launch_stream_lds(const KArgs &a, dim3 grid, hipStream_t s)
     QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 16),     \
     QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 32),     \
     X(FMT, BIT, SW, 16, 32, 4, 2, 1024),           \
-    X(FMT, BIT, SW, 32, 32, 8, 2, 1024)
+    X(FMT, BIT, SW, 32, 32, 8, 2, 1024),           \
+    X(FMT, BIT, SW, 32, 32, 4, 2, 512),            \
+    X(FMT, BIT, SW, 32, 32, 8, 4, 512)
 
 }  // namespace qlin
