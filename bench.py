@@ -7,9 +7,10 @@ already resident in HBM.  The default workload is W8A8_INT8 scaled_mm on the
 (6144,2048)} at every decode token count M in {1,2,4,8,16,24,32}: 28 GEMMs.
 
 Cold caches: every call of a step reads its own copy of the weights, and the
-copies rotate over three steps, so about 1 GiB of distinct weights passes
-through between two reads of the same copy; the 256 MB Infinity Cache and
-the L2s cannot serve them.  A step is captured once into a HIP graph per
+copies rotate over enough steps (four for this workload) that about 1 GiB of
+distinct weights passes through between two reads of the same copy; the
+256 MB Infinity Cache and the L2s cannot serve them.  The per-point timings
+rotate over ~1 GiB of copies of the point's own weights likewise.  A step is captured once into a HIP graph per
 rotation set and replayed (graph replay is also how the pages benchmark and
 deploy their kernels), so the time is GPU time, not Python launch overhead.
 
@@ -106,11 +107,39 @@ class Workload:
         self.weight_bytes = sum(it["N"] * it["K"] * self.sets for it in self.items)
 
     def call(self, it, s):
+        self.call_b(it, it["b"][s])
+
+    def call_b(self, it, b):
         q = self.q
         if it["fmt"] == "block_fp8":
-            q.block_scaled_mm(it["a"], it["sa"], it["b"][s], it["sb"], out=it["y"], config=it["cfg"])
+            q.block_scaled_mm(it["a"], it["sa"], b, it["sb"], out=it["y"], config=it["cfg"])
         else:
-            q.scaled_mm(it["a"], it["sa"], it["b"][s], it["sb"], out=it["y"], config=it["cfg"])
+            q.scaled_mm(it["a"], it["sa"], b, it["sb"], out=it["y"], config=it["cfg"])
+
+    def point_us(self, it, reps: int, cold_bytes: int = 1 << 30, max_copies: int = 256) -> float:
+        """Mean launch time of one point: a graph of at least `reps` launches,
+        each on the next of enough weight copies (the point's own plus
+        temporary clones) that ~`cold_bytes` of distinct weights pass between
+        two reads of one copy, so neither the Infinity Cache nor the L2s
+        serve the weights; replayed twice, timed with events on the launch
+        stream."""
+        import torch
+        n = int(min(max_copies, max(len(it["b"]), -(-cold_bytes // (it["N"] * it["K"])))))
+        bs = list(it["b"]) + [it["b"][0].clone() for _ in range(n - len(it["b"]))]
+        launches = max(reps, n)
+        g = capture(lambda: [self.call_b(it, bs[r % n]) for r in range(launches)])
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (2 * launches)
+        del g, bs
+        return us
 
     def step(self, s):
         for it in self.items:
@@ -125,7 +154,7 @@ def capture(fn):
     return g
 
 
-def run_gpu(wl: Workload, steps: int, warmup: int, reps: int):
+def run_gpu(wl: Workload, steps: int, warmup: int, reps: int, points: bool = True):
     import torch
 
     for i in range(max(1, warmup)):
@@ -147,23 +176,9 @@ def run_gpu(wl: Workload, steps: int, warmup: int, reps: int):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
 
-    # ---- per-kernel durations: a graph of `reps` launches per point, each on
-    # the next weight copy, timed with events on the launch stream.
-    per = []
-    for it in wl.items:
-        g = capture(lambda it=it: [wl.call(it, r % wl.sets) for r in range(reps)])
-        g.replay()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        g.replay()
-        g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / (2 * reps)
-        per.append(us)
-        del g
+    # ---- per-kernel durations, each point on its own with cold weights
+    per = [wl.point_us(it, reps) for it in wl.items] if points else []
+    torch.cuda.empty_cache()
     return ms, per
 
 
@@ -198,9 +213,9 @@ def cpu_baseline(wl: Workload, threads: int, budget_s: float):
 
 
 def prefill_points(reps: int = 4):
-    """Per-point GEMM time of the MFMA-bound (M >= 512) points: a graph of
-    `reps` launches per point on alternating weight copies, replayed twice,
-    timed with events on the launch stream."""
+    """Per-point GEMM time of the MFMA-bound (M >= 512) points, each with
+    cold weights (Workload.point_us: at least `reps` launches rotating over
+    ~1 GiB of weight copies, at most 64 of them)."""
     import torch
     wl = Workload("prefill", copies_target_bytes=0)
     for it in wl.items:                # eager calls size the split-K workspace before capture
@@ -208,18 +223,8 @@ def prefill_points(reps: int = 4):
     torch.cuda.synchronize()
     out = []
     for it in wl.items:
-        g = capture(lambda it=it: [wl.call(it, r % wl.sets) for r in range(reps)])
-        g.replay()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        g.replay()
-        g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / (2 * reps)
-        del g
+        us = wl.point_us(it, reps, max_copies=64)
+        torch.cuda.empty_cache()
         tf = it["flops"] / us / 1e6
         c = it["cfg"]
         out.append({"fmt": it["fmt"], "M": it["M"], "N": it["N"], "K": it["K"], "us": round(us, 2),
@@ -458,6 +463,9 @@ def main():
                     help="also run one 256 MiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--table", default=None, help="config table file to load before running")
     ap.add_argument("--per-point", action="store_true", help="print per-point timings to stderr")
+    ap.add_argument("--no-points", action="store_true",
+                    help="skip the per-point timings (counter runs: every point then "
+                         "launches equally often, as in a step)")
     ap.add_argument("--no-dispatch", action="store_true", help="skip the host dispatch-cost run")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M >= 512 per-point timings")
     ap.add_argument("--no-moe", action="store_true", help="skip the grouped (MoE) GEMM timings")
@@ -480,7 +488,7 @@ def main():
     wl = Workload(args.workload)
     log(f"workload {args.workload}: {len(wl.items)} GEMMs/step, {wl.bytes_per_step / 1e6:.1f} MB "
         f"algorithmic/step, {wl.sets} weight copies ({wl.weight_bytes / 2**30:.2f} GiB)")
-    ms, per_us = run_gpu(wl, args.steps, args.warmup, args.reps)
+    ms, per_us = run_gpu(wl, args.steps, args.warmup, args.reps, points=not args.no_points)
     ms_step = ms / args.steps
     value_tbs = wl.bytes_per_step / (ms_step * 1e-3) / 1e12
 
@@ -570,7 +578,7 @@ def main():
                                "algorithmic bytes per launch = mean over the step's GEMMs",
                      "alg_bytes_per_launch": round(launch_bytes, 1),
                      "launch_avg_us": round(launch_us, 3),
-                     "isolated_launch_avg_us": round(kern_us / len(per_us), 3),
+                     "isolated_launch_avg_us": round(kern_us / len(per_us), 3) if per_us else None,
                      "traffic_src": traffic_src},
         "cpu_baseline": cpu,
         "dispatch": dispatch,
