@@ -17,7 +17,7 @@ deploy their kernels), so the time is GPU time, not Python launch overhead.
 Metric: effective TB/s = algorithmic bytes / time, with algorithmic bytes
 M*K + N*K + 2*M*N + scale bytes per GEMM (each operand moved once).
 
-Prints ONE JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+Prints ONE JSON line.  --gpus N with N > 1 exits: the benchmark runs on one GPU.
 """
 from __future__ import annotations
 
@@ -474,7 +474,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1 "
                                    "(multi-GPU sharding is a design note, not a code path)"}))
         sys.exit(2)
 

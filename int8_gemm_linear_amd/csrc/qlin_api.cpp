@@ -253,7 +253,7 @@ qlin_status check_config(int fmt, int scal, int64_t M, int64_t N, int64_t K,
 // instance over 128-expert layers (K, N) = (2048, 1536) and (768, 2048) at
 // 1-52 rows per expert: the LDS-ring stream kernel with 8-token tiles up to
 // 3 rows, the register stream kernel with 16x64 tiles up to 16, a 64x128
-// tile up to 64 and a 128x128 tile beyond.  A choice this build lacks for
+// tile up to 64 and a 128x128 tile beyond.  A choice the library lacks for
 // the format falls back to the table's config with split_k = 1.
 qlin_config grouped_config(int fmt, int scal, int64_t M, int64_t N, int64_t K);
 
@@ -275,7 +275,7 @@ qlin_config select_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
     // decode config would re-stream the weights once per 16-32 tokens.
     if (!best && largest && !(M > 64 && M > 2 * largest->M))
         best = largest;
-    // An entry that does not fit this M (or names an instance this build
+    // An entry that does not fit this M (or names an instance the library
     // lacks) falls back to the built-in default rather than failing.
     if (best && check_config(fmt, scal, M, N, K, best->cfg, nullptr) == QLIN_OK)
         return best->cfg;
