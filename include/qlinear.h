@@ -99,9 +99,11 @@ typedef enum qlin_scaling {
 typedef enum qlin_kernel {
     QLIN_KERNEL_STREAM = 0,     /* weights streamed HBM -> registers; small M */
     QLIN_KERNEL_TILE = 1,       /* A and B tiles staged through a double-buffered LDS ring; large M */
-    QLIN_KERNEL_STREAM_LDS = 2  /* weights and tokens copied HBM -> LDS in 1 KB row segments
+    QLIN_KERNEL_STREAM_LDS = 2, /* weights and tokens copied HBM -> LDS in 1 KB row segments
                                    through a multi-stage ring; small M; K % 256 == 0;
                                    token/channel scaling only */
+    QLIN_KERNEL_GEMV = 3        /* one wave per weight row, dot products on the vector ALUs;
+                                   1-4 tokens; token/channel scaling only; split_k = 1 */
 } qlin_kernel;
 
 typedef enum qlin_variant {

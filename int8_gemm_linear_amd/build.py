@@ -34,6 +34,7 @@ SOURCES = [
     "qlin_tile_block.hip",
     "qlin_stream_lds_fp8.hip",
     "qlin_stream_lds_int8.hip",
+    "qlin_gemv.hip",
 ]
 
 ARCH = "gfx950"

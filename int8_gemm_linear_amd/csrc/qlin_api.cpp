@@ -54,7 +54,7 @@ const std::vector<Instance> &registry()
             stream_instances_fp8, stream_instances_int8, stream_instances_block,
             tile_instances_fp8, tile_instances_int8, tile_instances_block,
             stream_lds_instances_fp8, stream_lds_instances_int8,
-            tile_h_instances_fp8, tile_h_instances_int8,
+            tile_h_instances_fp8, tile_h_instances_int8, gemv_instances,
         };
         for (auto f : fns) {
             int n = 0;
@@ -324,6 +324,8 @@ qlin_status check_config(int fmt, int scal, int64_t M, int64_t N, int64_t K,
         return QLIN_ERR_BAD_CONFIG;   // the LDS ring copies whole 128-byte K steps
     if (c.kernel == QLIN_KERNEL_STREAM_LDS && (K % 256 != 0 || c.split_k > K / 256))
         return QLIN_ERR_BAD_CONFIG;   // 256-byte K units keep the LDS swizzle in range
+    if (c.kernel == QLIN_KERNEL_GEMV && c.split_k != 1)
+        return QLIN_ERR_BAD_CONFIG;   // a wave covers a weight row's whole K
     int64_t gx, gy;
     grid_of(c, M, N, &gx, &gy);
     if (gx > 0x7fffffff || gy > 65535)

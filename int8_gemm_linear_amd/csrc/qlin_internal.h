@@ -86,6 +86,7 @@ const Instance *tile_instances_int8(int *count);
 const Instance *tile_instances_block(int *count);
 const Instance *stream_lds_instances_fp8(int *count);
 const Instance *stream_lds_instances_int8(int *count);
+const Instance *gemv_instances(int *count);
 const Instance *tile_h_instances_fp8(int *count);
 const Instance *tile_h_instances_int8(int *count);
 

@@ -48,6 +48,8 @@ def candidates(fmt: str, M: int, N: int, K: int, max_split: int = 256):
             continue                      # the stream kernels are for small token counts
         if base.kernel == q.KERNEL_TILE and M < 16:
             continue
+        if base.kernel == q.KERNEL_GEMV and M > base.tile_m:
+            continue                      # one token tile per workgroup column
         split = 1
         while split <= min(max_split, 256):
             kw = base.waves_k if base.kernel == q.KERNEL_STREAM else 1

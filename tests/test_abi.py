@@ -95,6 +95,15 @@ def some_stream_cfg(fmt="int8"):
     raise AssertionError("no stream instance")
 
 
+def test_gemv_takes_no_split():
+    g = [c for c in q.instances_for("int8") if c.kernel == q.KERNEL_GEMV]
+    assert g, "no GEMV instance"
+    assert q.check_config("int8", 1, 2048, 2048, g[0]) == 0
+    assert q.check_config("int8", 1, 2048, 2048, g[0].replace(split_k=2)) == ST["cfg"]
+    assert smm(cfg=g[0].replace(split_k=2)) == ST["cfg"]               # rejected before any launch
+    assert not [c for c in q.instances_for("block_fp8") if c.kernel == q.KERNEL_GEMV]
+
+
 def test_explicit_config_errors():
     c = some_stream_cfg()
     assert smm(cfg=c.replace(split_k=3)) == ST["cfg"]
