@@ -49,7 +49,7 @@ def fingerprint(table_path: str | None = None) -> str:
 
 
 def _is_gemm(name: str) -> bool:
-    return "qlin::k_stream" in name or "qlin::k_tile" in name
+    return "qlin::k_stream" in name or "qlin::k_tile" in name or "qlin::k_gemv" in name
 
 
 def _is_qlin(name: str) -> bool:
