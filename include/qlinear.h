@@ -103,7 +103,7 @@ typedef enum qlin_kernel {
                                    through a multi-stage ring; small M; K % 256 == 0;
                                    token/channel scaling only */
     QLIN_KERNEL_GEMV = 3        /* one wave per weight row, dot products on the vector ALUs;
-                                   1-4 tokens; token/channel scaling only; split_k = 1 */
+                                   1-8 tokens; token/channel scaling only; split_k = 1 */
 } qlin_kernel;
 
 typedef enum qlin_variant {
