@@ -172,6 +172,18 @@ k_gemv(KArgs p_)
     // end reads the row's last piece and its token bytes are zeroed before
     // use; a batch past the last one (issued only to keep the code straight)
     // has every lane read the row's first 16 bytes, one cache line per wave.
+    // This lane's output (lane t * RPW + r stores (m0 + t, nw0 + r)) and its
+    // two scales, loaded now: read at the end they would add a memory round
+    // trip after the stream whenever the scale vectors are not in cache.
+    // Unpredicated, so in raw-accumulator mode (no scales) they read B.
+    const int t_out = min(lane / RPW, TMS - 1);
+    const int r_out = lane % RPW;
+    const bool scaled = p.acc_out == nullptr;
+    const float *sap = scaled ? p.sA : reinterpret_cast<const float *>(p.B);
+    const float *sbp = scaled ? p.sB : reinterpret_cast<const float *>(p.B);
+    const float sa_out = sap[scaled ? min(m0 + t_out, p.M - 1) : 0];
+    const float sb_out = sbp[scaled ? min(nw0 + r_out, p.N - 1) : 0];
+
     const int K = p.K;
     const int nb = (K + BK - 1) / BK;
     auto koff = [&](int b, int piece) { return b < nb ? min(b * BK + 16 * piece, K - 16) : 0; };
@@ -285,19 +297,20 @@ k_gemv(KArgs p_)
         for (int r = 0; r < RPW; ++r)
             acc[t][r] = wave_sum(acc[t][r]);
 
-    // Lane t * RPW + r stores output (m0 + t, nw0 + r).
-    const int t = lane / RPW;
-    const int r = lane % RPW;
-    if (lane >= TMS * RPW || m0 + t >= p.M || nw0 + r >= p.N)
+    if (lane >= TMS * RPW || m0 + t_out >= p.M || nw0 + r_out >= p.N)
         return;
     T v = acc[0][0];
 #pragma unroll
     for (int tt = 0; tt < TMS; ++tt)
 #pragma unroll
         for (int rr = 0; rr < RPW; ++rr)
-            if (tt == t && rr == r)
+            if (tt == t_out && rr == r_out)
                 v = acc[tt][rr];
-    store_final<FMT, SC_TC>(p, m0 + t, nw0 + r, v);
+    const int64_t t = m0 + t_out, n = nw0 + r_out;
+    if (scaled)
+        p.Y[t * p.ldy + n] = bf16_bits(((float)v * sa_out) * sb_out);   // as store_final
+    else
+        store_final<FMT, SC_TC>(p, (int)t, (int)n, v);
 }
 
 template <int FMT, int TMS, int RPW, int NW, int JB, bool SA>
