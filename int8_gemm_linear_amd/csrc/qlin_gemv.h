@@ -29,6 +29,7 @@
 #pragma once
 
 #include "qlin_device.h"
+#include "qlin_dpp.h"
 
 namespace qlin {
 
@@ -122,45 +123,6 @@ __device__ inline void dot_piece(const v4i (&w)[RPW], const v4i (&a)[TMS],
 __device__ inline v4i ld_global16(const uint8_t *p)
 {
     return *(const __attribute__((address_space(1))) v4i *)(p);
-}
-
-// Sum over the 64 lanes of a wave, returned to every lane.  Within each row
-// of 16 lanes four DPP moves pair lane i with i ^ 1, i ^ 2, then the mirror
-// lane of its half row and of its row (register-to-register, no LDS round
-// trip as a generic shuffle takes), leaving the row's sum in all 16 lanes;
-// the four row sums are then read out and added in row order.  Integer sums
-// are exact in any order; fp32 sums take this fixed order in every call.
-__device__ inline int dpp_pair(int v, int ctrl_sel)
-{
-    // 0xB1: quad_perm [1,0,3,2]; 0x4E: quad_perm [2,3,0,1];
-    // 0x141: row_half_mirror; 0x140: row_mirror.
-    switch (ctrl_sel) {
-    case 0: return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
-    case 1: return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
-    case 2: return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);
-    default: return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);
-    }
-}
-
-__device__ inline int32_t wave_sum(int32_t v)
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        v += dpp_pair(v, i);
-    return ((__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
-            __builtin_amdgcn_readlane(v, 32)) + __builtin_amdgcn_readlane(v, 48);
-}
-
-__device__ inline float wave_sum(float v)
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        v += __int_as_float(dpp_pair(__float_as_int(v), i));
-    const int vi = __float_as_int(v);
-    return ((__int_as_float(__builtin_amdgcn_readlane(vi, 0)) +
-             __int_as_float(__builtin_amdgcn_readlane(vi, 16))) +
-            __int_as_float(__builtin_amdgcn_readlane(vi, 32))) +
-           __int_as_float(__builtin_amdgcn_readlane(vi, 48));
 }
 
 template <int FMT, int TMS, int RPW, int NW, int JB, bool SA>

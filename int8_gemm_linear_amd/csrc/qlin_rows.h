@@ -20,6 +20,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "qlin_dpp.h"
 #include "qlin_quant.h"
 
 namespace qlin {
@@ -171,9 +172,7 @@ __device__ inline u32x4 silu8(u32x4 gw, u32x4 uw)
 template <int W>
 __device__ inline double row_sum(double v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        v += __shfl_xor(v, o, 64);
+    v = wave_sum(v);
     if constexpr (W > 1) {
         __shared__ double red[kMaxW];
         if ((threadIdx.x & 63) == 0)
@@ -190,9 +189,7 @@ __device__ inline double row_sum(double v)
 template <int W>
 __device__ inline float row_max(float v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        v = fmaxf(v, __shfl_xor(v, o, 64));
+    v = wave_max(v);
     if constexpr (W > 1) {
         __shared__ float red[kMaxW];
         if ((threadIdx.x & 63) == 0)
@@ -219,10 +216,7 @@ __device__ inline void quantize_row(const u32x4 (&y)[kReg], int P, uint8_t *qrow
         // P is a multiple of 16: the 16 lanes of a group are all active or
         // all idle, so the 16-wide butterfly stays inside the group
         auto emit = [&](const u32x4 &v, int p) {
-            float m = amax8(v);
-#pragma unroll
-            for (int o = 8; o >= 1; o >>= 1)
-                m = fmaxf(m, __shfl_xor(m, o, 16));
+            const float m = row16_max(amax8(v));
             const float s = span_scale<false>(m);
             q[p] = quant8<false>(v, s);
             if ((t & 15) == 0)
