@@ -661,6 +661,7 @@ hipError_t launch_tile(const KArgs &a, dim3 grid, hipStream_t s)
     X(FMT, SCAL, BIT, SW, 64, 128, 1, 4, 4),    \
     X(FMT, SCAL, BIT, SW, 128, 128, 2, 2, 2),   \
     X(FMT, SCAL, BIT, SW, 128, 128, 2, 2, 4),   \
+    X(FMT, SCAL, BIT, SW, 128, 128, 4, 2, 4),   \
     X(FMT, SCAL, BIT, SW, 128, 256, 2, 2, 3),   \
     X(FMT, SCAL, BIT, SW, 256, 128, 2, 2, 3),   \
     X(FMT, SCAL, BIT, SW, 256, 256, 2, 2, 2),   \
