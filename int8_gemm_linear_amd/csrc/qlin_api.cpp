@@ -251,10 +251,12 @@ qlin_status check_config(int fmt, int scal, int64_t M, int64_t N, int64_t K,
 // Grouped (mixture-of-experts) calls: split_k = 1 (grid.z is the expert)
 // and a kernel chosen by the bound on rows per expert, from a sweep of every
 // instance over 128-expert layers (K, N) = (2048, 1536) and (768, 2048) at
-// 1-52 rows per expert: the LDS-ring stream kernel with 8-token tiles up to
-// 3 rows, the register stream kernel with 16x64 tiles up to 16, a 64x128
-// tile up to 64 and a 128x128 tile beyond.  A choice the library lacks for
-// the format falls back to the table's config with split_k = 1.
+// 1-52 rows per expert: up to 3 rows the GEMV kernel when K >= 2048 (one or
+// two token rows per tile; at K = 768 its 2 KB row batches are mostly idle
+// lanes) and otherwise the LDS-ring stream kernel with 8-token tiles, the
+// register stream kernel with 16x64 tiles up to 16, a 64x128 tile up to 64
+// and a 128x128 tile beyond.  A choice the library lacks for the format
+// falls back to the table's config with split_k = 1.
 qlin_config grouped_config(int fmt, int scal, int64_t M, int64_t N, int64_t K);
 
 qlin_config select_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
@@ -295,12 +297,15 @@ qlin_config grouped_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
         c.reduce = QLIN_REDUCE_LAST_ARRIVER;
         return c;
     };
-    const qlin_config pick =
-        M <= 3    ? make(QLIN_KERNEL_STREAM_LDS, 8, 16, 512, 1, 4, 4)
+    qlin_config pick =
+        M <= 3 && K >= 2048 && scal == SC_TC ? make(QLIN_KERNEL_GEMV, M == 1 ? 1 : 2, 8, 2048, 1, 4, 2)
+        : M <= 3  ? make(QLIN_KERNEL_STREAM_LDS, 8, 16, 512, 1, 4, 4)
         : M <= 16 ? make(QLIN_KERNEL_STREAM, 16, 64, 128, 1, 4, 2)
         : M <= 64 ? (scal == SC_TC ? make(QLIN_KERNEL_TILE, 64, 128, 128, 1, 4, 4)
                                    : make(QLIN_KERNEL_TILE, 64, 128, 128, 1, 4, 2))
                   : make(QLIN_KERNEL_TILE, 128, 128, 128, 2, 2, 2);
+    if (pick.kernel == QLIN_KERNEL_GEMV)
+        pick.variant = QLIN_STANDARD;     // the GEMV kernel has no Swap-AB form
     if (check_config(fmt, scal, M, N, K, pick, nullptr) == QLIN_OK)
         return pick;
     qlin_config c = select_config(fmt, scal, M, N, K);

@@ -338,3 +338,7 @@ def test_grouped_default_config_is_valid_and_unsplit():
                 c = q.select_grouped_config(fmt, mr, N, K)
                 assert c.split_k == 1, (fmt, mr, c)
                 assert q.check_config(fmt, mr, N, K, c) == 0, (fmt, mr, N, K, c)
+                # the rule: GEMV for at most 3 rows per expert at K >= 2048
+                # (token/channel formats), the LDS-ring kernel below that K
+                if mr <= 3 and fmt != "block_fp8":
+                    assert c.kernel == (q.KERNEL_GEMV if K >= 2048 else q.KERNEL_STREAM_LDS), (fmt, mr, K, c)

@@ -121,6 +121,22 @@ def test_every_instance_grouped(fmt):
             assert np.array_equal(y, first), f"int8 instance disagreement at {c}"
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("max_rows", [1, 2, 3])
+def test_few_rows_per_expert_default_kernel(fmt, max_rows):
+    # decode routing with at most 3 rows per expert at K >= 2048: the
+    # default grouped choice (the GEMV kernel) against the oracle
+    sizes = [min(max_rows, s) for s in (1, 0, 3, 2, 1, 0, 3)]
+    N, K = 384, 2048
+    c = q.select_grouped_config(fmt, max_rows, N, K)
+    say(fmt, "few rows", max_rows, c)
+    assert c.kernel == q.KERNEL_GEMV
+    qa, sa, qb, sb, off = moe_case(fmt, sizes, N, K, seed=6)
+    dev = to_dev(fmt, qa, sa, qb, sb, off)
+    y = run(fmt, dev, max_rows)
+    check(fmt, y, qa, sa, qb, sb, off, max_rows, f"{fmt} few rows {max_rows}")
+
+
 def test_max_rows_caps_each_group():
     # rows of a group past max_rows are left untouched (documented bound)
     sizes = [5, 9, 0, 12]
