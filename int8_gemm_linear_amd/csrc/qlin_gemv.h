@@ -44,33 +44,12 @@ struct GemvAcc<FMT_E4M3> {
     typedef float T;
 };
 
-// acc += <w, a> over 16 bytes (16 int8 or 16 e4m3 values).
-template <int FMT>
-__device__ inline typename GemvAcc<FMT>::T dot16(v4i w, v4i a, typename GemvAcc<FMT>::T acc);
-
-template <>
-__device__ inline int32_t dot16<FMT_INT8>(v4i w, v4i a, int32_t acc)
+// acc += <w, a> over 16 int8 bytes.
+__device__ inline int32_t dot16_i8(v4i w, v4i a, int32_t acc)
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         acc = __builtin_amdgcn_sdot4(w[i], a[i], acc, false);
-    return acc;
-}
-
-template <>
-__device__ inline float dot16<FMT_E4M3>(v4i w, v4i a, float acc)
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const v2f w0 = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
-        const v2f w1 = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
-        const v2f a0 = __builtin_amdgcn_cvt_pk_f32_fp8(a[i], false);
-        const v2f a1 = __builtin_amdgcn_cvt_pk_f32_fp8(a[i], true);
-        acc = __builtin_fmaf(w0[0], a0[0], acc);
-        acc = __builtin_fmaf(w0[1], a0[1], acc);
-        acc = __builtin_fmaf(w1[0], a1[0], acc);
-        acc = __builtin_fmaf(w1[1], a1[1], acc);
-    }
     return acc;
 }
 
@@ -86,7 +65,7 @@ __device__ inline void dot_piece(const v4i (&w)[RPW], const v4i (&a)[TMS],
         for (int t = 0; t < TMS; ++t)
 #pragma unroll
             for (int r = 0; r < RPW; ++r)
-                acc[t][r] = dot16<FMT_INT8>(w[r], a[t], acc[t][r]);
+                acc[t][r] = dot16_i8(w[r], a[t], acc[t][r]);
     } else {
         float wf[RPW][16];
 #pragma unroll

@@ -227,9 +227,15 @@ k_stream_lds(KArgs p_)
     }
 
     // Combine the waves' partial sums in fixed order (wave 0 first); the ring
-    // is free once every wave has passed this barrier.
+    // is free once every wave has passed this barrier.  Without split-K the
+    // combine is spread over the waves (below): wave w sums and stores the
+    // accumulator elements e with e % NW == w, so no wave reads all the
+    // others' partials in sequence.  Same order of additions either way.
     __syncthreads();
-    if (NW > 1) {
+    constexpr int E = RB * TB * 4;                   // accumulator elements per lane
+    constexpr bool SPREAD = NW > 1 && NW * E * 64 * 4 <= S * STAGE;
+    const bool spread = SPREAD && p.split_k == 1;
+    if (NW > 1 && !spread) {
         AS *red = reinterpret_cast<AS *>(lds);      // [NW-1][RB*TB*4][64]
         static_assert((NW - 1) * RB * TB * 4 * 64 * 4 <= S * STAGE, "reduction space");
         if (wave > 0) {
@@ -305,6 +311,42 @@ k_stream_lds(KArgs p_)
             }
     };
 
+    if (spread) {
+        AS *red = reinterpret_cast<AS *>(lds);      // [NW][E][64]
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    red[(wave * E + (rb * TB + tb) * 4 + v) * 64 + lane] = acc[rb][tb][v];
+        __syncthreads();
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int e = (rb * TB + tb) * 4 + v;
+                    if (e % NW != wave)
+                        continue;
+                    AS sum = red[e * 64 + lane];
+#pragma unroll
+                    for (int w = 1; w < NW; ++w)
+                        sum += red[(w * E + e) * 64 + lane];
+                    const int t = SWAP ? m0 + tb * 16 + r16 : m0 + tb * 16 + 4 * g + v;
+                    const int n = SWAP ? n0 + rb * 16 + 4 * g + v : n0 + rb * 16 + r16;
+                    if (t >= mend || n >= nend)
+                        continue;
+                    if (!scaled)
+                        store_final<FMT, SC_TC>(p, t, n, sum);
+                    else
+                        p.Y[(int64_t)t * p.ldy + n] =
+                            bf16_bits(((float)sum * (SWAP ? sa1[tb] : sa4[tb][v])) *
+                                      (SWAP ? sb4[rb][v] : sb1[rb]));
+                }
+        return;
+    }
     if (p.split_k == 1) {
         if (wave == 0)
             emit(acc);
