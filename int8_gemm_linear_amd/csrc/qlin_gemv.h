@@ -1,5 +1,5 @@
-// The GEMV kernel family: 1-8 tokens with token/channel scaling, on the
-// vector ALUs instead of the matrix cores.
+// The GEMV kernel family: 1-8 tokens (token/channel scaling) or 1-2 tokens
+// (Block_FP8), on the vector ALUs instead of the matrix cores.
 //
 // Why: at one to eight tokens a decode GEMM does 2-16 flops per weight byte,
 // so the matrix cores idle whatever the kernel does, and what remains is the
@@ -104,11 +104,13 @@ __device__ inline v4i ld_global16(const uint8_t *p)
     return *(const __attribute__((address_space(1))) v4i *)(p);
 }
 
-template <int FMT, int TMS, int RPW, int NW, int JB, bool SA>
+template <int FMT, int TMS, int RPW, int NW, int JB, bool SA, int SCAL>
 __global__ void __launch_bounds__(64 * NW)
 k_gemv(KArgs p_)
 {
     typedef typename GemvAcc<FMT>::T T;
+    constexpr bool BLK = SCAL == SC_BLOCK;           // Block_FP8: scales per 128-wide K group
+    static_assert(!BLK || (FMT == FMT_E4M3 && !SA), "block scaling: e4m3, token rows per wave");
     static_assert(TMS >= 1 && TMS <= 8 && RPW >= 1 && RPW <= 2 && JB >= 1 && JB <= 8, "shape");
     static_assert(TMS * RPW <= 64, "one output per lane");
     constexpr int BK = 1024 * JB;                    // K bytes per batch
@@ -117,7 +119,7 @@ k_gemv(KArgs p_)
     static_assert(!SA || (TMS * PB) % (64 * NW) == 0, "token copies split evenly");
 
     KArgs p = p_;
-    if (p.group_off && !enter_group<SC_TC>(p))
+    if (p.group_off && !enter_group<SCAL>(p))
         return;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -147,7 +149,7 @@ k_gemv(KArgs p_)
     // Unpredicated, so in raw-accumulator mode (no scales) they read B.
     const int t_out = min(lane / RPW, TMS - 1);
     const int r_out = lane % RPW;
-    const bool scaled = p.acc_out == nullptr;
+    const bool scaled = p.acc_out == nullptr && !BLK;
     const float *sap = scaled ? p.sA : reinterpret_cast<const float *>(p.B);
     const float *sbp = scaled ? p.sB : reinterpret_cast<const float *>(p.B);
     const float sa_out = sap[scaled ? min(m0 + t_out, p.M - 1) : 0];
@@ -181,6 +183,25 @@ k_gemv(KArgs p_)
     };
 
     v4i w0[RPW][JB], a0[TMS][JB], w1[RPW][JB], a1[TMS][JB];
+    // Block_FP8: the scales of each piece's 128-wide K group (weight block
+    // row n / 128, token row), loaded with the piece, one set per batch.
+    float gw0[BLK ? RPW : 1][BLK ? JB : 1], gx0[BLK ? TMS : 1][BLK ? JB : 1];
+    float gw1[BLK ? RPW : 1][BLK ? JB : 1], gx1[BLK ? TMS : 1][BLK ? JB : 1];
+    auto load_group_scales = [&](int b, float (&gw)[BLK ? RPW : 1][BLK ? JB : 1],
+                                 float (&gx)[BLK ? TMS : 1][BLK ? JB : 1]) {
+        if constexpr (BLK) {
+#pragma unroll
+            for (int j = 0; j < JB; ++j) {
+                const int grp = koff(b, j * 64 + lane) >> 7;
+#pragma unroll
+                for (int r = 0; r < RPW; ++r)
+                    gw[r][j] = p.sB[(int64_t)(min(nw0 + r, p.N - 1) >> 7) * p.G + grp];
+#pragma unroll
+                for (int t = 0; t < TMS; ++t)
+                    gx[t][j] = p.sA[(int64_t)min(m0 + t, p.M - 1) * p.G + grp];
+            }
+        }
+    };
     auto load = [&](int b, v4i (&w)[RPW][JB], v4i (&a)[TMS][JB]) {
         load_a_shared(b);                            // before the weights: waited for first
         if constexpr (SA)
@@ -204,7 +225,9 @@ k_gemv(KArgs p_)
 #pragma unroll
         for (int r = 0; r < RPW; ++r)
             acc[t][r] = 0;
-    auto use = [&](int b, int buf, const v4i (&w)[RPW][JB], const v4i (&a)[TMS][JB]) {
+    auto use = [&](int b, int buf, const v4i (&w)[RPW][JB], const v4i (&a)[TMS][JB],
+                   const float (&gw)[BLK ? RPW : 1][BLK ? JB : 1],
+                   const float (&gx)[BLK ? TMS : 1][BLK ? JB : 1]) {
 #pragma unroll
         for (int j = 0; j < JB; ++j) {
             v4i wj[RPW], aj[TMS];
@@ -221,7 +244,24 @@ k_gemv(KArgs p_)
                 for (int t = 0; t < TMS; ++t)
                     aj[t] = ok ? a[t][j] : zero4i();
             }
-            dot_piece<FMT, TMS, RPW>(wj, aj, acc);
+            if constexpr (BLK) {
+                // acc += (group piece product) * sA * sB, the promotion of
+                // the block kernels applied per 16-value piece
+                T d[TMS][RPW];
+#pragma unroll
+                for (int t = 0; t < TMS; ++t)
+#pragma unroll
+                    for (int r = 0; r < RPW; ++r)
+                        d[t][r] = 0;
+                dot_piece<FMT, TMS, RPW>(wj, aj, d);
+#pragma unroll
+                for (int t = 0; t < TMS; ++t)
+#pragma unroll
+                    for (int r = 0; r < RPW; ++r)
+                        acc[t][r] = __builtin_fmaf(d[t][r], gx[t][j] * gw[r][j], acc[t][r]);
+            } else {
+                dot_piece<FMT, TMS, RPW>(wj, aj, acc);
+            }
         }
     };
 
@@ -230,19 +270,22 @@ k_gemv(KArgs p_)
     // batch's token pieces go to LDS after the previous batch is used, then
     // one barrier publishes them (and retires the buffer read before).
     if (nb == 1) {
+        load_group_scales(0, gw0, gx0);
         load(0, w0, a0);
         store_a_shared(0, 0);
         if (SA)
             __syncthreads();
-        use(0, 0, w0, a0);
+        use(0, 0, w0, a0, gw0, gx0);
     } else {
+        load_group_scales(0, gw0, gx0);
         load(0, w0, a0);
         store_a_shared(0, 0);
         if (SA)
             __syncthreads();
         for (int b = 0; b < nb; b += 2) {
+            load_group_scales(b + 1, gw1, gx1);
             load(b + 1, w1, a1);
-            use(b, 0, w0, a0);
+            use(b, 0, w0, a0, gw0, gx0);
             if (SA) {
                 if (b + 1 < nb)
                     store_a_shared(b + 1, 1);
@@ -250,8 +293,9 @@ k_gemv(KArgs p_)
             }
             if (b + 1 >= nb)
                 break;
+            load_group_scales(b + 2, gw0, gx0);
             load(b + 2, w0, a0);
-            use(b + 1, 1, w1, a1);
+            use(b + 1, 1, w1, a1, gw1, gx1);
             if (SA) {
                 if (b + 2 < nb)
                     store_a_shared(b + 2, 0);
@@ -279,13 +323,13 @@ k_gemv(KArgs p_)
     if (scaled)
         p.Y[t * p.ldy + n] = bf16_bits(((float)v * sa_out) * sb_out);   // as store_final
     else
-        store_final<FMT, SC_TC>(p, (int)t, (int)n, v);
+        store_final<FMT, SCAL>(p, (int)t, (int)n, v);
 }
 
-template <int FMT, int TMS, int RPW, int NW, int JB, bool SA>
+template <int FMT, int TMS, int RPW, int NW, int JB, bool SA, int SCAL>
 hipError_t launch_gemv(const KArgs &a, dim3 grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_gemv<FMT, TMS, RPW, NW, JB, SA>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((k_gemv<FMT, TMS, RPW, NW, JB, SA, SCAL>), grid, dim3(64 * NW), 0, s, a);
     return hipGetLastError();
 }
 
@@ -295,7 +339,19 @@ hipError_t launch_gemv(const KArgs &a, dim3 grid, hipStream_t s)
 // through two LDS buffers as well); split_k = 1 only.
 #define QLIN_GEMV_INSTANCE(FMT, BIT, TMS, RPW, NW, JB, SA)                                      \
     {{QLIN_KERNEL_GEMV, 0, TMS, (NW) * (RPW), 1024 * (JB), 1, NW, (SA) ? 4 : 2, 1, 0}, BIT, FMT, \
-     SC_TC, &launch_gemv<FMT, TMS, RPW, NW, JB, SA>}
+     SC_TC, &launch_gemv<FMT, TMS, RPW, NW, JB, SA, SC_TC>}
+#define QLIN_GEMV_BLOCK_INSTANCE(TMS, RPW, NW, JB)                                              \
+    {{QLIN_KERNEL_GEMV, 0, TMS, (NW) * (RPW), 1024 * (JB), 1, NW, 2, 1, 0}, FB_BLOCK, FMT_E4M3,   \
+     SC_BLOCK, &launch_gemv<FMT_E4M3, TMS, RPW, NW, JB, false, SC_BLOCK>}
+
+// Block_FP8 (token rows read by every wave).
+#define QLIN_GEMV_BLOCK_SHAPES(X) \
+    X(1, 1, 4, 2),                \
+    X(1, 1, 8, 2),                \
+    X(1, 2, 4, 2),                \
+    X(1, 1, 4, 4),                \
+    X(2, 1, 4, 2),                \
+    X(2, 2, 4, 2)
 
 #define QLIN_GEMV_SHAPES(X, FMT, BIT)  \
     X(FMT, BIT, 1, 1, 4, 2, false),    \

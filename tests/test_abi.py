@@ -101,7 +101,8 @@ def test_gemv_takes_no_split():
     assert q.check_config("int8", 1, 2048, 2048, g[0]) == 0
     assert q.check_config("int8", 1, 2048, 2048, g[0].replace(split_k=2)) == ST["cfg"]
     assert smm(cfg=g[0].replace(split_k=2)) == ST["cfg"]               # rejected before any launch
-    assert not [c for c in q.instances_for("block_fp8") if c.kernel == q.KERNEL_GEMV]
+    blk = [c for c in q.instances_for("block_fp8") if c.kernel == q.KERNEL_GEMV]
+    assert blk and all(c.tile_m <= 2 and c.stages == 2 for c in blk)
 
 
 def test_explicit_config_errors():
