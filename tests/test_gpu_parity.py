@@ -114,6 +114,29 @@ def test_k_not_multiple_of_128(fmt):
         parity.check_case(case, y)
 
 
+@pytest.mark.parametrize("fmt", ["int8", "fp8", "block_fp8"])
+def test_gemv_ragged_k_and_rows(fmt):
+    # every GEMV instance at 1-2 tokens on K that ends inside a 1 KB row
+    # segment (and, token/channel formats, inside a 128-byte step), N not a
+    # multiple of the rows per workgroup: pieces past K are zeroed, rows past
+    # N are never stored
+    shapes = ((1, 77, 1040), (2, 130, 2064), (1, 33, 6160)) if fmt != "block_fp8" else \
+             ((1, 256, 1152), (2, 384, 2176), (1, 128, 6272))
+    gemv = [c for c in q.instances_for(fmt) if c.kernel == q.KERNEL_GEMV]
+    assert gemv
+    for M, N, K in shapes:
+        case = small_case(fmt, M, N, K, root=29)
+        dev = parity.to_device(case)
+        ref = parity.oracle_full(case)
+        for c in gemv:
+            if q.check_config(fmt, M, N, K, c) != 0:
+                continue
+            say(fmt, "gemv", (M, N, K), c)
+            y = call(case, dev, c)
+            torch.cuda.synchronize()
+            parity.check_case(case, y, ref, what=f"{fmt} {c} {(M, N, K)}")
+
+
 def test_split_k_sweep():
     M, N, K = 24, 512, 4096
     for fmt in ("int8", "fp8", "block_fp8"):
