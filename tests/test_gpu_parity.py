@@ -223,6 +223,34 @@ def test_output_stride_and_guard_bands():
             assert (g == 0x7777).all(), "write outside the output view"
 
 
+@pytest.mark.parametrize("fmt", ["int8", "fp8", "block_fp8"])
+def test_gemv_strided_operands_and_guard_bands(fmt):
+    # every GEMV instance with lda > K, ldb > K and an output view inside a
+    # guarded buffer: results as the oracle's, nothing written outside
+    M, N, K = 2, 256, 2048
+    case = small_case(fmt, M, N, K, root=31)
+    a, sa, b, sb = parity.to_device(case)
+    ap = torch.zeros((M, K + 48), dtype=torch.uint8, device="cuda")
+    bp = torch.zeros((N, K + 32), dtype=torch.uint8, device="cuda")
+    ap[:, :K] = a.view(torch.uint8)
+    bp[:, :K] = b.view(torch.uint8)
+    a2, b2 = ap.view(a.dtype)[:, :K], bp.view(b.dtype)[:, :K]
+    ref = parity.oracle_full(case)
+    for c in [c for c in q.instances_for(fmt) if c.kernel == q.KERNEL_GEMV]:
+        if q.check_config(fmt, M, N, K, c) != 0:
+            continue
+        big = torch.full((M + 2, N + 40), 0x7777, dtype=torch.int16, device="cuda")
+        out = big.view(torch.bfloat16)[1:M + 1, 8:8 + N]
+        say("gemv strides", fmt, c)
+        f = q.block_scaled_mm if case.block else q.scaled_mm
+        f(a2, sa, b2, sb, out=out, config=c)
+        torch.cuda.synchronize()
+        parity.check_case(case, out.contiguous(), ref, what=f"{fmt} {c}")
+        g = big.cpu().numpy().copy()
+        g[1:M + 1, 8:8 + N] = 0x7777
+        assert (g == 0x7777).all(), f"write outside the output view: {c}"
+
+
 def test_hip_graph_capture_and_replay():
     M, N, K = 16, 2048, 2048
     for fmt in ("int8", "fp8", "block_fp8"):
