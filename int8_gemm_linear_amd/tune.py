@@ -14,7 +14,8 @@ graph of R launches, each on a different copy of the weights (together
 larger than the 256 MB Infinity Cache, so weights come from HBM), replayed a
 few times; the per-launch time is the median replay time / R.  A candidate
 whose output differs from the reference candidate's is discarded (INT8: bit
-for bit; FP8: relative difference above 2^-6).
+for bit; FP8: a normwise difference above 1e-2, or an element further than
+2^-5 of the output's largest magnitude).
 
     python -m int8_gemm_linear_amd.tune --workload int8_1p7b_decode \
         --jsonl tune.jsonl --table int8_gemm_linear_amd/configs/qlin_mi355x.cfg

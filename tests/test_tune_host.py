@@ -1,0 +1,46 @@
+"""Host-side checks of the tuner's candidate set (CPU only): which kernel
+families and splits it offers per token count, and that every candidate is
+a configuration the library accepts for the point."""
+import int8_gemm_linear_amd as q
+from int8_gemm_linear_amd.tune import candidates
+
+
+def kinds(cands):
+    return {c.kernel for c in cands}
+
+
+def test_every_candidate_is_accepted():
+    for fmt, M, N, K in (("int8", 1, 2048, 2048), ("fp8", 24, 4096, 4096),
+                         ("block_fp8", 2, 5120, 8192), ("fp8", 2048, 5120, 8192)):
+        cands = candidates(fmt, M, N, K)
+        assert cands, (fmt, M, N, K)
+        for c in cands:
+            assert q.check_config(fmt, M, N, K, c) == 0, (fmt, M, N, K, c)
+
+
+def test_token_count_decides_the_families():
+    one = candidates("int8", 1, 2048, 2048)
+    assert q.KERNEL_GEMV in kinds(one) and q.KERNEL_STREAM_LDS in kinds(one)
+    assert q.KERNEL_TILE not in kinds(one)                   # tiles start at 16 tokens
+    # GEMV only for token counts its tile covers in one workgroup column
+    for M in (1, 2, 4, 8, 16):
+        for c in candidates("int8", M, 2048, 2048):
+            if c.kernel == q.KERNEL_GEMV:
+                assert M <= c.tile_m, (M, c)
+    big = candidates("fp8", 2048, 5120, 8192)
+    assert kinds(big) == {q.KERNEL_TILE}                      # stream kernels stop at 4 token tiles
+
+
+def test_gemv_candidates_take_no_split():
+    for fmt in ("int8", "fp8", "block_fp8"):
+        g = [c for c in candidates(fmt, 1, 4096, 4096) if c.kernel == q.KERNEL_GEMV]
+        assert g, fmt
+        assert all(c.split_k == 1 for c in g), fmt
+
+
+def test_splits_are_powers_of_two_within_the_k_steps():
+    K = 2048
+    for c in candidates("int8", 8, 2048, K):
+        s = c.split_k
+        assert s & (s - 1) == 0 and 1 <= s <= 256
+        assert s <= K // 128
