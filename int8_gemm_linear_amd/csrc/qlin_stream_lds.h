@@ -8,7 +8,7 @@
 // The LDS round trip costs nothing that matters here: LDS bandwidth is far
 // above a CU's share of HBM bandwidth.
 //
-// Workgroup: NW waves own TR = 8, 16, 32 or 64 weight rows (the matrix core sees
+// Workgroup: NW waves own TR = 8, 16, 32, 48 or 64 weight rows (the matrix core sees
 // blocks of 16; with 8 rows, fragment rows 8..15 repeat rows 0..7 and their
 // outputs are dropped, which doubles the workgroup count for small N without
 // a split-K reduction) and TMS tokens (1..32; the
@@ -65,7 +65,7 @@ k_stream_lds(KArgs p_)
     constexpr int TR = TRW;                          // weight rows of the workgroup
     constexpr int RB = TR >= 16 ? TR / 16 : 1;       // 16-row matrix-core blocks
     constexpr int RMASK = TR >= 16 ? 15 : TR - 1;    // fragment row within the stage
-    static_assert(TR == 8 || TR == 16 || TR == 32 || TR == 64, "weight rows");
+    static_assert(TR == 8 || TR == 16 || TR == 32 || TR == 48 || TR == 64, "weight rows");
     constexpr int RPI = 1024 / CHK;                  // rows per load instruction
     constexpr int ROWS0 = TR + TMS;
     constexpr int INSTR = ((ROWS0 + RPI * NW - 1) / (RPI * NW)) * NW;   // padded
@@ -432,6 +432,8 @@ hipError_t launch_stream_lds(const KArgs &a, dim3 grid, hipStream_t s)
     X(FMT, BIT, SW, 32, 32, 8, 2, 1024),           \
     X(FMT, BIT, SW, 32, 32, 4, 2, 512),            \
     X(FMT, BIT, SW, 32, 32, 8, 4, 512),            \
-    X(FMT, BIT, SW, 32, 64, 8, 3, 512)
+    X(FMT, BIT, SW, 32, 64, 8, 3, 512),            \
+    X(FMT, BIT, SW, 16, 48, 8, 3, 512),            \
+    X(FMT, BIT, SW, 32, 48, 8, 3, 512)
 
 }  // namespace qlin
