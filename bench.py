@@ -242,13 +242,15 @@ def prefill_points(reps: int = 4):
 
 # Activation producers upstream of the GEMM (quantizers and fused norm /
 # activation + quantizer), at the decode (M = 32) and prefill (M = 2048)
-# sizes of the 8B- and 32B-class models: (op, M, K).  Algorithmic bytes:
-# every input and output moved once (bf16 2 B, codes 1 B, fp32 scales).
+# sizes of the 8B- and 32B-class models, plus SiLU-and-mul at the decode
+# size of the 1.7B-class model (intermediate 6144): (op, M, K).  Algorithmic
+# bytes: every input and output moved once (bf16 2 B, codes 1 B, fp32 scales).
 PRODUCER_POINTS = [
     ("quant_per_token", 32, 4096), ("quant_per_token", 2048, 5120),
     ("quant_per_group128", 2048, 5120),
     ("rms_norm_dynamic_per_token_quant", 32, 4096), ("rms_norm_dynamic_per_token_quant", 2048, 5120),
     ("rms_norm_per_block_quant", 2048, 5120),
+    ("silu_and_mul_dynamic_per_token_quant", 32, 6144),
     ("silu_and_mul_dynamic_per_token_quant", 32, 12288),
     ("silu_and_mul_dynamic_per_token_quant", 2048, 25600),
     ("silu_and_mul_per_block_quant", 2048, 25600),

@@ -7,7 +7,8 @@
 // at the bandwidth is latency hiding, so a row is as few waves as fit it in
 // registers (W = 1 for rows up to 4096 values, 2 up to 8192, ... 8 up to
 // 32768) when there are rows enough to fill the machine, more (up to 8)
-// when there are not: every lane issues all its 16-byte loads (kReg
+// when there are not (quantizer and RMS norm; SiLU-and-mul rows keep the
+// fewest, see silu_waves): every lane issues all its 16-byte loads (kReg
 // pieces) before it uses any, a single-wave row reduces with shuffles
 // alone, and small workgroups let many rows be in flight per CU.  Lane t of the row owns the
 // pieces t, t + 64W, ...; pieces beyond the register window (rows longer
@@ -344,16 +345,31 @@ inline int waves_for(int64_t M, int64_t K)
     return w;
 }
 
+// Waves per SiLU-and-mul row: only the fewest that hold the row's pieces in
+// registers, at most 4.  Every lane runs all kReg register slots, and a
+// slot past the row's end (zeros) takes the exact double-precision path
+// (zero fails the fast path's range test), so spreading a short row over
+// more waves lengthens each lane's chain instead of shortening it
+// (measured, same codes and scales: M = 32, K = 4096 on one wave 11.9 us,
+// on four 21.5 us; M = 1 10.4 against 20.6 us).  At most 4: the kernels
+// need ~125 registers, so an 8-wave workgroup would leave room for only one
+// per CU; longer rows recompute the pieces past the register window
+// (measured faster: 113 vs 134 us at 2048 x 25600).
+inline int silu_waves(int64_t K)
+{
+    const int64_t P = K >> 3;
+    int w = 1;
+    while (w < 4 && (int64_t)64 * w * kReg < P)
+        w *= 2;
+    return w;
+}
+
 template <int OP, int QM, bool RES>
 hipError_t launch_rows(const RowArgs &a, int64_t M, hipStream_t s)
 {
     const dim3 grid((unsigned)M);
-    // SiLU-and-mul rows take at most 4 waves: its kernels need ~125
-    // registers, so an 8-wave workgroup would leave room for only one per
-    // CU; longer rows recompute the pieces past the register window
-    // (measured faster: 113 vs 134 us at 2048 x 25600).
-    const int w = waves_for(M, a.K);
-    switch (OP == OP_SILU && w > 4 ? 4 : w) {
+    const int w = OP == OP_SILU ? silu_waves(a.K) : waves_for(M, a.K);
+    switch (w) {
     case 1: hipLaunchKernelGGL((k_rows<OP, QM, 1, RES>), grid, dim3(64), 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_rows<OP, QM, 2, RES>), grid, dim3(128), 0, s, a); break;
     case 4: hipLaunchKernelGGL((k_rows<OP, QM, 4, RES>), grid, dim3(256), 0, s, a); break;
