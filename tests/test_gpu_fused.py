@@ -83,8 +83,10 @@ def test_rms_norm_quant_bit_exact(fmt, block, M, K, with_residual):
 
 
 @pytest.mark.parametrize("fmt,block", [("fp8", False), ("int8", False), ("fp8", True)])
+# wave counts 1 (K <= 4096; K = 4096 fills every register slot), 2 (6144)
+# and 4 (12288 up, past the register window from 16384)
 @pytest.mark.parametrize("M,K", [(1, 128), (7, 6144), (33, 12288), (2, 25600), (3, 40960),
-                                 (64, 2048)])
+                                 (64, 2048), (32, 4096)])
 def test_silu_and_mul_quant_bit_exact(fmt, block, M, K):
     say("silu", fmt, "block" if block else "token", M, K)
     x = act(M, 2 * K, scale=2.0)
