@@ -64,3 +64,23 @@ def test_traffic_record_is_dropped_when_the_kernels_change(tmp_path):
     assert profsum.fingerprint(str(other)) != profsum.fingerprint(None)
     traffic, why = bench.load_traffic("int8_1p7b_decode", str(other))
     assert traffic is None and "changed" in why
+
+
+def test_producer_bytes_count_every_operand_once():
+    # per value: bf16 input 2 B, code 1 B; SiLU-and-mul reads gate and up
+    # (4 B); the RMS norm also reads and writes the residual (2 + 2 B) and
+    # reads the bf16 weight once; fp32 scales per row or per 1x128 group
+    M, K = 32, 4096
+    row_scales, group_scales = 4 * M, 4 * M * (K // 128)
+    assert bench.producer_bytes("quant_per_token", M, K) == 3 * M * K + row_scales
+    assert bench.producer_bytes("quant_per_group128", M, K) == 3 * M * K + group_scales
+    assert bench.producer_bytes("rms_norm_dynamic_per_token_quant", M, K) == (
+        7 * M * K + 2 * K + row_scales)
+    assert bench.producer_bytes("rms_norm_per_block_quant", M, K) == 7 * M * K + 2 * K + group_scales
+    assert bench.producer_bytes("silu_and_mul_dynamic_per_token_quant", M, K) == 5 * M * K + row_scales
+    assert bench.producer_bytes("silu_and_mul_per_block_quant", M, K) == 5 * M * K + group_scales
+    # every producer the bench line times is one of these
+    assert {op for (op, _, _) in bench.PRODUCER_POINTS} == {
+        "quant_per_token", "quant_per_group128", "rms_norm_dynamic_per_token_quant",
+        "rms_norm_per_block_quant", "silu_and_mul_dynamic_per_token_quant",
+        "silu_and_mul_per_block_quant"}
