@@ -91,3 +91,30 @@ def gemm_exact(fmt: str, A, sA, B, sB, block: bool = False):
                 acc[m][n] = tot
                 y[m][n] = ysum
     return y, acc
+
+
+def bound_exact(fmt: str, A, sA, B, sB, block: bool = False):
+    """Exact bound matrix S[m][n] as Fractions: the sum over k of
+    |a[m,k] b[n,k]| times |sA[m]| |sB[n]| (token / channel scales), or for
+    1x128 / 128x128 block scales the sum over K groups g of
+    |sA[m,g]| |sB[n//128,g]| times the group's sum of |a b|."""
+    A = np.asarray(A).view(np.uint8)
+    B = np.asarray(B).view(np.uint8)
+    M, K = A.shape
+    N = B.shape[0]
+    da = [[abs(decode(fmt, int(c))) for c in row] for row in A]
+    db = [[abs(decode(fmt, int(c))) for c in row] for row in B]
+    S = [[None] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            if not block:
+                s = sum((da[m][k] * db[n][k] for k in range(K)), Fraction(0))
+                S[m][n] = s * abs(Fraction(float(sA[m]))) * abs(Fraction(float(sB[n])))
+            else:
+                tot = Fraction(0)
+                for g in range(K // 128):
+                    p = sum((da[m][k] * db[n][k] for k in range(g * 128, g * 128 + 128)),
+                            Fraction(0))
+                    tot += p * abs(Fraction(float(sA[m][g]))) * abs(Fraction(float(sB[n // 128][g])))
+                S[m][n] = tot
+    return S

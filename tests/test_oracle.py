@@ -309,6 +309,128 @@ def test_bound_matrix():
     assert np.allclose(r2.bound, r2.ydbl, rtol=1e-14, atol=0)
 
 
+# --------------------------------------------------------------------------
+# The bound matrix S (the scale of the elementwise FP8 / Block_FP8 rule):
+# |sum ab| in place of sum |ab|, a missing |.| on a scale, a Block bound
+# paired with the wrong group or weight block row, a constant factor.
+# --------------------------------------------------------------------------
+def _abs_decoded(fmt, codes):
+    """|value| of each code, decoded by torch's casts (not by the oracle)."""
+    c = np.ascontiguousarray(codes).view(np.uint8)
+    if fmt == "int8":
+        return np.abs(c.view(np.int8).astype(np.int64))
+    return np.abs(torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy())
+
+
+def _tiny_mixed_case(fmt, M, N, K, seed):
+    """Random codes of both signs (no NaN codes) and scales of both signs."""
+    g = np.random.default_rng(seed)
+    if fmt == "int8":
+        A = g.integers(-128, 128, (M, K)).astype(np.int8).view(np.uint8)
+        B = g.integers(-128, 128, (N, K)).astype(np.int8).view(np.uint8)
+    else:
+        A = (g.integers(0, 0x7F, (M, K)) | (g.integers(0, 2, (M, K)) << 7)).astype(np.uint8)
+        B = (g.integers(0, 0x7F, (N, K)) | (g.integers(0, 2, (N, K)) << 7)).astype(np.uint8)
+    if fmt == "block_fp8":
+        sA = (g.uniform(0.01, 2, (M, K // 128)) * g.choice([-1, 1], (M, K // 128))).astype(np.float32)
+        sB = (g.uniform(0.01, 2, (N // 128, K // 128)) * g.choice([-1, 1], (N // 128, K // 128))
+              ).astype(np.float32)
+    else:
+        sA = (g.uniform(0.01, 2, M) * g.choice([-1, 1], M)).astype(np.float32)
+        sB = (g.uniform(0.01, 2, N) * g.choice([-1, 1], N)).astype(np.float32)
+    return A, sA, B, sB
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [("fp8", 3, 5, 48), ("int8", 3, 5, 48),
+                                       ("block_fp8", 2, 256, 256)])
+def test_bound_matrix_exact_rationals(fmt, M, N, K):
+    A, sA, B, sB = _tiny_mixed_case(fmt, M, N, K, seed=17)
+    block = fmt == "block_fp8"
+    r = oracle.scaled_mm(FMT[fmt], A, sA, B, sB, block=block)
+    # Block: a few outputs on each side of the weight-block boundary at n = 128
+    cols = (0, 1, 127, 128, 200, 255) if block else range(N)
+    for m in range(M):
+        for n in cols:
+            if block:
+                nb = n // 128
+                exact = brute.bound_exact(fmt, A[m:m + 1], sA[m:m + 1], B[n:n + 1],
+                                          sB[nb:nb + 1], block=True)[0][0]
+            else:
+                exact = brute.bound_exact(fmt, A[m:m + 1], sA[m:m + 1], B[n:n + 1],
+                                          sB[n:n + 1])[0][0]
+            got = Fraction(float(r.bound[m, n]))
+            assert abs(got - exact) <= exact * Fraction(1, 2 ** 50), (fmt, m, n, float(exact), float(got))
+    # cancellation really happens in these inputs: the bound exceeds |y| by a wide margin somewhere
+    assert (r.bound > 2 * np.abs(r.ydbl)).any()
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8", "block_fp8"])
+def test_bound_matrix_numpy(fmt):
+    # The workloads' value distributions at a size spanning several weight
+    # blocks; S recomputed from torch-decoded magnitudes with numpy products.
+    # Every e4m3 product is a multiple of 2^-18 and every int8 product an
+    # integer, so the sums of magnitudes are exact in float64 in any order and
+    # the scaling is the same two roundings in the same order: bit-exact.
+    case = synth.make_case(fmt, 12, 384, 1024, root=18)
+    r = run(case)
+    a, b = _abs_decoded(fmt, case.A), _abs_decoded(fmt, case.B)
+    if fmt != "block_fp8":
+        P = (a.astype(np.float64) @ b.astype(np.float64).T)
+        S = (P * np.abs(case.sA.astype(np.float64))[:, None]) * np.abs(case.sB.astype(np.float64))[None, :]
+    else:
+        G = case.K // 128
+        S = np.zeros((case.M, case.N))
+        nb = np.arange(case.N) // 128
+        for g in range(G):
+            P = a[:, g * 128:(g + 1) * 128] @ b[:, g * 128:(g + 1) * 128].T
+            sa = np.abs(case.sA[:, g].astype(np.float64))[:, None]
+            sb = np.abs(case.sB[nb, g].astype(np.float64))[None, :]
+            S = S + (P * sa) * sb
+    assert np.array_equal(r.bound, S)
+
+
+def test_bound_matrix_block_all_positive_equals_y():
+    # Block_FP8 with positive codes and scales: no cancellation anywhere, so S == y
+    case = synth.make_case("block_fp8", 5, 256, 512, root=19)
+    A = case.A & 0x7F
+    B = case.B & 0x7F
+    r = oracle.scaled_mm(oracle.FMT_E4M3, A, case.sA, B, case.sB, block=True)
+    assert np.array_equal(r.bound, r.ydbl)
+    # ... and flipping the sign of one operand's codes leaves S unchanged
+    r2 = oracle.scaled_mm(oracle.FMT_E4M3, A | 0x80, case.sA, B, case.sB, block=True)
+    assert np.array_equal(r2.bound, r.bound)
+    assert np.array_equal(r2.ydbl, -r.ydbl)
+
+
+def test_bound_golden_cancellation():
+    with open(os.path.join(HERE, "golden", "bound_examples.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        M, N, K = c["M"], c["N"], c["K"]
+        A = np.zeros((M, K), np.int64)
+        for row, k, code in c["A"]:
+            A[row, k] = code
+        B = np.zeros((N, K), np.int64)
+        if "B" in c:
+            for row, k, code in c["B"]:
+                B[row, k] = code
+        else:
+            for k, code in c["B_all_rows"]:
+                B[:, k] = code
+        A = A.astype(np.int8).view(np.uint8) if c["fmt"] == "int8" else A.astype(np.uint8)
+        B = B.astype(np.int8).view(np.uint8) if c["fmt"] == "int8" else B.astype(np.uint8)
+        r = oracle.scaled_mm(FMT[c["fmt"]], A, np.array(c["sA"], np.float32), B,
+                             np.array(c["sB"], np.float32), block=c["block"])
+        if "S" in c:
+            assert r.bound.tolist() == c["S"], c["name"]
+            assert r.ydbl.tolist() == c["y"], c["name"]
+        else:
+            for blk, (yv, sv) in enumerate(zip(c["y_by_block"], c["S_by_block"])):
+                cols = slice(blk * 128, (blk + 1) * 128)
+                assert (r.bound[:, cols] == sv).all(), (c["name"], blk)
+                assert (r.ydbl[:, cols] == yv).all(), (c["name"], blk)
+
+
 def test_points_mode_equals_full():
     case = synth.make_case("block_fp8", 7, 256, 512, root=15)
     full = run(case)
