@@ -2,14 +2,18 @@
 
 A step is one pass of the hot path over a whole workload: one scaled_mm /
 block_scaled_mm call per (format, M, N, K) point, each on the weight matrix
-already resident in HBM.  The default workload is W8A8_INT8 scaled_mm on the
-1.7B-class decoder linears (K, N) in {(2048,4096), (2048,2048), (2048,12288),
-(6144,2048)} at every decode token count M in {1,2,4,8,16,24,32}: 28 GEMMs.
+already resident in HBM.  The default workload is the largest decode
+configuration: FP8_Dynamic, W8A8_INT8 and Block_FP8 on the 32B-class decoder
+linears (K, N) in {(5120,10240), (8192,5120), (5120,51200), (25600,5120)} at
+every decode token count M in {1,2,4,8,16,24,32}: 84 GEMMs.  The same line
+also reports the W8A8_INT8 1.7B-class decode workload (28 GEMMs) and the
+M >= 512 points (TFLOP/s).
 
 Cold caches: every call of a step reads its own copy of the weights, and the
-copies rotate over enough steps (four for this workload) that about 1 GiB of
-distinct weights passes through between two reads of the same copy; the
-256 MB Infinity Cache and the L2s cannot serve them.  The per-point timings
+copies rotate over enough steps that about 1 GiB of distinct weights passes
+through between two reads of the same copy (a step of the default workload
+alone reads 10 GB of weights); the 256 MB Infinity Cache and the L2s cannot
+serve them.  The per-point timings
 rotate over ~1 GiB of copies of the point's own weights likewise.  A step is captured once into a HIP graph per
 rotation set and replayed (graph replay is also how the pages benchmark and
 deploy their kernels), so the time is GPU time, not Python launch overhead.
@@ -44,6 +48,8 @@ WORKLOAD_TEXT = {
     "block_fp8_8b": "Block_FP8 block_scaled_mm, 8B-class linears x M in {1,2,4,8,16,24,32,512}",
     "all_32b": "FP8_Dynamic, W8A8_INT8 and Block_FP8 on 32B-class linears (K,N) in "
                "{(5120,10240),(8192,5120),(5120,51200),(25600,5120)} x M in {1,2,4,8,16,24,32,2048}",
+    "all_32b_decode": "FP8_Dynamic, W8A8_INT8 and Block_FP8 on 32B-class linears (K,N) in "
+                      "{(5120,10240),(8192,5120),(5120,51200),(25600,5120)} x M in {1,2,4,8,16,24,32}",
     "fp8_small": "FP8_Dynamic scaled_mm, M=16 N=512 K=1024",
     "prefill": "the M >= 512 points: FP8_Dynamic and Block_FP8 8B-class at M=512, all three "
                "formats on the 32B-class linears at M=2048",
@@ -452,12 +458,57 @@ def load_traffic(workload: str, table: str | None):
     return rec["traffic_bytes_per_call"], os.path.relpath(path, ROOT)
 
 
+def oracle_threads() -> tuple[int, dict]:
+    """Threads for the oracle timing: every host CPU this process may run on,
+    capped by OMP_NUM_THREADS when set (the host's CPU share per GPU)."""
+    nproc = os.cpu_count() or 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = nproc
+    cap = os.environ.get("OMP_NUM_THREADS")
+    threads = avail
+    if cap and cap.isdigit() and int(cap) > 0:
+        threads = min(threads, int(cap))
+    return max(1, threads), {"nproc": nproc, "affinity_cpus": avail, "omp_num_threads": cap}
+
+
+def step_timing(wl: "Workload", steps: int, warmup: int, reps: int, points: bool):
+    """Time `steps` steps of a workload; returns a dict of the step-level figures
+    plus the per-point launch times (empty without points)."""
+    ms, per_us = run_gpu(wl, steps, warmup, reps, points=points)
+    ms_step = ms / steps
+    n_launch = len(wl.items)
+    launch_bytes = wl.bytes_per_step / n_launch
+    launch_us = ms_step * 1e3 / n_launch
+    return {"ms_step": ms_step, "value_tbs": wl.bytes_per_step / (ms_step * 1e-3) / 1e12,
+            "launch_bytes": launch_bytes, "launch_us": launch_us,
+            "achieved_gbs": launch_bytes / (launch_us * 1e-6) / 1e9,
+            "flops_tops": wl.flops_per_step / (ms_step * 1e-3) / 1e12}, per_us
+
+
+def per_format(wl: "Workload", per_us) -> dict:
+    """TB/s and fraction of 8 TB/s per format, from the per-point times."""
+    out = {}
+    for fmt in ("fp8", "int8", "block_fp8"):
+        pts = [(it, us) for it, us in zip(wl.items, per_us) if it["fmt"] == fmt]
+        if not pts:
+            continue
+        b = sum(it["bytes"] for it, _ in pts)
+        t = sum(us for _, us in pts)
+        tbs = b / t / 1e6
+        geo = float(np.exp(np.mean([np.log(it["bytes"] / us / 1e6) for it, us in pts])))
+        out[fmt] = {"points": len(pts), "tbs": round(tbs, 4), "frac": round(tbs / 8.0, 4),
+                    "geomean_tbs": round(geo, 4), "sum_us": round(t, 2)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="int8_1p7b_decode", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--workload", default="all_32b_decode", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--reps", type=int, default=24, help="launches per point in the kernel-timing graphs")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu", action="store_true")
@@ -473,6 +524,8 @@ def main():
     ap.add_argument("--no-moe", action="store_true", help="skip the grouped (MoE) GEMM timings")
     ap.add_argument("--no-producers", action="store_true",
                     help="skip the activation-producer timings (quantizers, fused norm / SiLU)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the W8A8_INT8 1.7B-class decode workload reported beside the headline")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -490,16 +543,8 @@ def main():
     wl = Workload(args.workload)
     log(f"workload {args.workload}: {len(wl.items)} GEMMs/step, {wl.bytes_per_step / 1e6:.1f} MB "
         f"algorithmic/step, {wl.sets} weight copies ({wl.weight_bytes / 2**30:.2f} GiB)")
-    ms, per_us = run_gpu(wl, args.steps, args.warmup, args.reps, points=not args.no_points)
-    ms_step = ms / args.steps
-    value_tbs = wl.bytes_per_step / (ms_step * 1e-3) / 1e12
-
-    # per launch over the timed region: the step is one graph of back-to-back
-    # GEMM launches on one stream, so its event time / launches is the mean
-    # launch duration (the rocprofv3 kernel trace of the same command agrees)
-    n_launch = len(wl.items)
-    launch_bytes = wl.bytes_per_step / n_launch
-    launch_us = ms_step * 1e3 / n_launch
+    head, per_us = step_timing(wl, args.steps, args.warmup, args.reps, points=not args.no_points)
+    log(f"step {head['ms_step'] * 1e3:.1f} us, {head['value_tbs']:.3f} TB/s")
     kern_us = sum(per_us)
     traffic, traffic_src = load_traffic(args.workload, args.table)
     if args.per_point:
@@ -508,7 +553,7 @@ def main():
             log(f"  {it['fmt']:9s} M={it['M']:5d} N={it['N']:6d} K={it['K']:6d}  {us:8.2f} us  "
                 f"{it['bytes'] / us / 1e6:7.3f} TB/s  {it['flops'] / us / 1e6:8.1f} TFLOP/s  "
                 f"k={c.kernel} v={c.variant} t={c.tile_m}x{c.tile_n}x{c.tile_k} "
-                f"w={c.waves_n}x{c.waves_k} s={c.split_k} r={c.reduce}")
+                f"w={c.waves_n}x{c.waves_k} st={c.stages} s={c.split_k} r={c.reduce}")
 
     if args.copy_calib:
         # a plain elementwise copy of known size: reads 256 MiB, writes 256 MiB
@@ -516,12 +561,13 @@ def main():
         dst = torch.empty_like(src)
         torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     parity_ok = None
     if not args.no_cpu:
         from tests import parity as par
-        threads = max(1, min(16, os.cpu_count() or 1))
+        threads, host = oracle_threads()
         done_bytes, done_flops, secs, n_calls, first = cpu_baseline(wl, threads, args.cpu_budget)
         # the GPU outputs of the last replayed step vs the oracle
         parity_ok = True
@@ -534,13 +580,31 @@ def main():
         b1, _, s1, n1, _ = cpu_baseline(wl, 1, args.cpu_budget / 3)
         cpu = {"value": done_bytes / secs / 1e12, "unit": "TB/s", "cores": threads,
                "kind": "oracle",
-               "sample": f"{n_calls} GEMM calls ({n_calls / len(wl.items):.1f} passes over the "
-                         f"{len(wl.items)} GEMMs of the workload, whole GEMMs), {secs:.1f} s on "
-                         f"{threads} threads (plain C, double/int64 accumulate)",
+               "sample": f"{n_calls} GEMM calls ({n_calls / len(wl.items):.2f} passes over the "
+                         f"{len(wl.items)} GEMMs of the workload, in order, whole GEMMs), {secs:.1f} s "
+                         f"on {threads} threads (plain C, double/int64 accumulate)",
                "single_thread_value": b1 / s1 / 1e12,
                "single_thread_sample": f"{n1} GEMM calls, {s1:.1f} s on 1 thread",
                "gflops": round(done_flops / secs / 1e9, 2),
-               "host_cpu": cpu_model()}
+               "host_cpu": cpu_model(), **host,
+               "parity_checked_gemms": len(first)}
+    points_fmt = per_format(wl, per_us) if per_us else None
+    wl_items = len(wl.items)
+    wl_bytes = wl.bytes_per_step
+    del wl
+    torch.cuda.empty_cache()
+
+    extra = None
+    if not args.no_extra and args.workload != "int8_1p7b_decode":
+        w2 = Workload("int8_1p7b_decode")
+        e, per2 = step_timing(w2, args.steps, args.warmup, args.reps, points=not args.no_points)
+        extra = {"workload": WORKLOAD_TEXT["int8_1p7b_decode"], "gemms_per_step": len(w2.items),
+                 "value": round(e["value_tbs"], 4), "unit": "TB/s", "ms_per_step": round(e["ms_step"], 5),
+                 "launch_avg_us": round(e["launch_us"], 3),
+                 "frac": round(e["achieved_gbs"] / HBM_PEAK_GBS, 4),
+                 "isolated_launch_avg_us": round(sum(per2) / len(per2), 3) if per2 else None}
+        del w2
+        torch.cuda.empty_cache()
 
     dispatch = None if args.no_dispatch else dispatch_cost()
     prefill = None
@@ -554,35 +618,36 @@ def main():
     if not args.no_moe and args.workload != "prefill":
         moe = moe_points()
 
-    flops_tops = wl.flops_per_step / (ms_step * 1e-3) / 1e12
+    fmts = {it[0] for it in synth_points(args.workload)}
     out = {
         "metric": "effective TB/s (M<=32) and TFLOPS (M>=512) for FP8/INT8 scaled GEMM, 1 GPU",
-        "value": round(value_tbs, 4),
+        "value": round(head["value_tbs"], 4),
         "unit": "TB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": round(head["ms_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8" if args.workload == "int8_1p7b_decode" else "e4m3/int8",
+        "dtype": "int8" if fmts == {"int8"} else "e4m3/int8",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.workload], "gemms_per_step": len(wl.items),
-                   "alg_bytes_per_step": wl.bytes_per_step, "tflops": round(flops_tops, 2),
-                   "weights_rotated_gib": round(wl.weight_bytes / 2**30, 3),
-                   "timing": "HIP-graph replay of whole steps, hipEvents"},
-        "roofline": {"bound": "hbm", "achieved": round(launch_bytes / (launch_us * 1e-6) / 1e9, 1),
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "gemms_per_step": wl_items,
+                   "alg_bytes_per_step": wl_bytes, "tflops": round(head["flops_tops"], 2),
+                   "timing": "HIP-graph replay of whole steps, hipEvents, cold weights"},
+        "roofline": {"bound": "hbm", "achieved": round(head["achieved_gbs"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(launch_bytes / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "frac": round(head["achieved_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "kernel": "the GEMM launch (kernel instance per shape from the tuned table); "
                                "algorithmic bytes per launch = mean over the step's GEMMs",
-                     "alg_bytes_per_launch": round(launch_bytes, 1),
-                     "launch_avg_us": round(launch_us, 3),
+                     "alg_bytes_per_launch": round(head["launch_bytes"], 1),
+                     "launch_avg_us": round(head["launch_us"], 3),
                      "isolated_launch_avg_us": round(kern_us / len(per_us), 3) if per_us else None,
                      "traffic_src": traffic_src},
+        "per_format": points_fmt,
         "cpu_baseline": cpu,
+        "int8_1p7b_decode": extra,
         "dispatch": dispatch,
         "prefill_mfma": prefill,
         "producers": producers,
@@ -590,6 +655,11 @@ def main():
         "parity_vs_oracle": parity_ok,
     }
     print(json.dumps(out), flush=True)
+
+
+def synth_points(name: str):
+    import synth
+    return synth.workload(name)
 
 
 if __name__ == "__main__":

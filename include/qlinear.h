@@ -58,8 +58,9 @@
  *    call writes partials into it, so one workspace serves every config.
  *    Calls that may overlap in time (different streams) need distinct
  *    workspaces.
- *  - Threading: concurrent calls are safe; qlin_load_config_table must not
- *    run concurrently with calls.
+ *  - Threading: concurrent calls are safe, qlin_load_config_table included:
+ *    a call that overlaps a table replacement uses either the old or the new
+ *    table (replaced tables stay in host memory until the process ends).
  */
 #ifndef QLINEAR_H
 #define QLINEAR_H
@@ -103,7 +104,8 @@ typedef enum qlin_kernel {
                                    through a multi-stage ring; small M; K % 256 == 0;
                                    token/channel scaling only */
     QLIN_KERNEL_GEMV = 3        /* one wave per weight row, dot products on the vector ALUs;
-                                   1-8 tokens; token/channel scaling only; split_k = 1 */
+                                   1-8 tokens (token/channel scaling) or 1-2 tokens
+                                   (block scaling); split_k = 1 */
 } qlin_kernel;
 
 typedef enum qlin_variant {
@@ -320,6 +322,14 @@ int32_t qlin_config_table_size(void);
 
 const char *qlin_status_string(qlin_status s);
 int32_t qlin_abi_version(void);
+
+/* Stream-capture state of `stream` (a hipStream_t; NULL is the null stream),
+ * for callers that keep one split-K workspace per HIP graph: returns 1 and
+ * sets *capture_id to the id of the capture in progress (unique per capture
+ * within the process), 0 (and *capture_id = 0) when the stream is not
+ * capturing, or -1 when the query fails or capture_id is NULL.  Launches
+ * nothing and does not synchronise. */
+int32_t qlin_stream_capture_id(void *stream, unsigned long long *capture_id);
 
 #ifdef __cplusplus
 }

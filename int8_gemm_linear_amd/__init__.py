@@ -131,6 +131,8 @@ def _lib():
     lib.qlin_status_string.restype = ctypes.c_char_p
     lib.qlin_abi_version.argtypes = []
     lib.qlin_abi_version.restype = ctypes.c_int32
+    lib.qlin_stream_capture_id.argtypes = [P, ctypes.POINTER(ctypes.c_ulonglong)]
+    lib.qlin_stream_capture_id.restype = ctypes.c_int32
     lib.qlin_quant_per_token.argtypes = [I, I64, I64, P, I64, P, I64, P, P]
     lib.qlin_quant_per_token.restype = I
     lib.qlin_quant_per_group128.argtypes = [I64, I64, P, I64, P, I64, P, P]
@@ -162,27 +164,51 @@ def lib():
 
 
 # ---------------------------------------------------------------------------
-# Workspace: one zeroed device buffer per device, grown on demand (its split-K
-# counter region is left zeroed by every call).  Calls that may run
-# concurrently on different streams must pass their own `workspace=`.  It is
-# never grown while a HIP graph is being captured: make one eager call with
-# the same shape first, or pass a workspace.
+# Split-K workspaces.  A workspace's counter region must hold zeros before
+# its first use, and a HIP graph keeps using the workspace address it was
+# captured with, so:
+#  * eager calls use one zeroed buffer per (device, stream): calls on
+#    different streams never share one;
+#  * each graph capture gets buffers of its own, allocated and zeroed inside
+#    the capture (torch's allocator serves them from the graph's pool and the
+#    zero fill is a kernel node that runs before the first call of every
+#    replay), so eager calls and other graphs never touch them;
+#  * a buffer is never freed once a call has used it: when a call needs more,
+#    a larger one replaces it and the old one is kept, because a graph
+#    captured earlier may still replay with its address.
+# Calls that may overlap in time on one stream cannot exist; graphs that may
+# replay concurrently on different streams were captured separately and hold
+# separate buffers.  A caller may always pass its own `workspace=` instead.
 # ---------------------------------------------------------------------------
 _WS: dict = {}
+_WS_KEPT: list = []
+
+
+def _capture_id(stream) -> int:
+    cid = ctypes.c_ulonglong(0)
+    r = _lib().qlin_stream_capture_id(ctypes.c_void_p(stream.cuda_stream), ctypes.byref(cid))
+    if r < 0:
+        raise RuntimeError("could not query the stream's capture state")
+    return int(cid.value) if r == 1 else 0
 
 
 def workspace_for(nbytes: int, device: torch.device, stream=None) -> torch.Tensor | None:
+    """A zeroed-counter workspace of at least `nbytes` for calls on `stream`
+    (the device's current stream by default)."""
     if nbytes == 0:
         return None
-    key = device.index if device.index is not None else torch.cuda.current_device()
+    dev = device.index if device.index is not None else torch.cuda.current_device()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    key = (dev, int(stream.cuda_stream), _capture_id(stream))
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
-        if torch.cuda.is_current_stream_capturing():
-            raise RuntimeError("the split-K workspace would have to grow during HIP graph capture; "
-                               "run the call once eagerly first or pass workspace=")
-        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
-        torch.cuda.current_stream(device).synchronize()
-        _WS[key] = buf
+        size = max(nbytes, 1 << 20, 2 * buf.numel() if buf is not None else 0)
+        with torch.cuda.stream(stream):
+            new = torch.zeros(size, dtype=torch.uint8, device=torch.device("cuda", dev))
+        if buf is not None:
+            _WS_KEPT.append(buf)
+        _WS[key] = buf = new
     return buf
 
 

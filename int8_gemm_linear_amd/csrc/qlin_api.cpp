@@ -10,11 +10,13 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cctype>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <fstream>
+#include <memory>
 #include <mutex>
 #include <sstream>
 #include <string>
@@ -91,10 +93,16 @@ struct Entry {
     qlin_config cfg;
 };
 
-std::vector<Entry> g_table;
-bool g_table_ready = false;
-std::mutex g_table_mutex;
-int g_log = -1;
+// The table in use.  A lookup reads it through an acquire load and never
+// takes a lock; a replacement installs a new table and keeps every earlier
+// one alive until the process ends, so a lookup that raced a replacement
+// still reads valid memory (tables are a few KB and replaced rarely).
+typedef std::vector<Entry> Table;
+std::atomic<const Table *> g_table{nullptr};
+std::once_flag g_table_once;
+std::mutex g_table_mutex;                       // serialises replacements
+std::vector<std::unique_ptr<Table>> g_tables;   // every table installed so far
+std::atomic<int> g_log{0};
 
 bool parse_table(const std::string &text, std::vector<Entry> &out)
 {
@@ -133,32 +141,36 @@ bool parse_table(const std::string &text, std::vector<Entry> &out)
     return true;
 }
 
-void ensure_table()
+void install_table(Table t)
 {
-    if (g_table_ready)
-        return;
     std::lock_guard<std::mutex> lk(g_table_mutex);
-    if (g_table_ready)
-        return;
-    if (g_log < 0) {
+    g_tables.push_back(std::unique_ptr<Table>(new Table(std::move(t))));
+    g_table.store(g_tables.back().get(), std::memory_order_release);
+}
+
+// First use: QLIN_LOG, then the table from QLIN_CONFIG when it names a
+// readable, well-formed file, else the compiled-in one.
+const Table &table()
+{
+    std::call_once(g_table_once, [] {
         const char *e = std::getenv("QLIN_LOG");
-        g_log = (e && *e && *e != '0') ? 1 : 0;
-    }
-    std::vector<Entry> t;
-    bool ok = false;
-    const char *path = std::getenv("QLIN_CONFIG");
-    if (path && *path) {
-        std::ifstream f(path);
-        if (f) {
-            std::stringstream ss;
-            ss << f.rdbuf();
-            ok = parse_table(ss.str(), t);
+        g_log.store((e && *e && *e != '0') ? 1 : 0, std::memory_order_relaxed);
+        Table t;
+        bool ok = false;
+        const char *path = std::getenv("QLIN_CONFIG");
+        if (path && *path) {
+            std::ifstream f(path);
+            if (f) {
+                std::stringstream ss;
+                ss << f.rdbuf();
+                ok = parse_table(ss.str(), t);
+            }
         }
-    }
-    if (!ok)
-        parse_table(kDefaultTable, t);
-    g_table.swap(t);
-    g_table_ready = true;
+        if (!ok)
+            parse_table(kDefaultTable, t);
+        install_table(std::move(t));
+    });
+    return *g_table.load(std::memory_order_acquire);
 }
 
 int ilog2_exact(int v)
@@ -261,10 +273,9 @@ qlin_config grouped_config(int fmt, int scal, int64_t M, int64_t N, int64_t K);
 
 qlin_config select_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
 {
-    ensure_table();
     const int bit = fmt_bit(fmt, scal);
     const Entry *best = nullptr, *largest = nullptr;
-    for (const Entry &e : g_table) {
+    for (const Entry &e : table()) {
         if (e.bit != bit || e.N != N || e.K != K)
             continue;
         if (e.M >= M && (!best || e.M < best->M))
@@ -420,7 +431,7 @@ qlin_status run(const Problem &pb, const qlin_config *cfg_in)
         if (!aligned(pb.ws, 16))
             return QLIN_ERR_MISALIGNED;
     }
-    if (g_log > 0)
+    if (g_log.load(std::memory_order_relaxed) > 0)
         std::fprintf(stderr,
                      "[qlinear] fmt=%d scal=%d M=%lld N=%lld K=%lld -> kernel=%d variant=%d "
                      "tile=%dx%dx%d waves=%dx%d stages=%d split_k=%d reduce=%d\n",
@@ -619,7 +630,6 @@ qlin_status qlin_select_grouped_config(qlin_scaling sc, qlin_dtype dt, int64_t m
         return QLIN_ERR_BAD_ARGUMENT;
     if (!out)
         return QLIN_ERR_NULL_POINTER;
-    ensure_table();
     *out = grouped_config(fmt, sc == QLIN_BLOCK128 ? SC_BLOCK : SC_TC, max_rows, N, K);
     return QLIN_OK;
 }
@@ -675,16 +685,14 @@ qlin_status qlin_load_config_table(const char *path)
         if (!parse_table(ss.str(), t))
             return QLIN_ERR_CONFIG_FILE;
     }
-    ensure_table();
-    std::lock_guard<std::mutex> lk(g_table_mutex);
-    g_table.swap(t);
+    table();            // the first-use load must not replace this table later
+    install_table(std::move(t));
     return QLIN_OK;
 }
 
 int32_t qlin_config_table_size(void)
 {
-    ensure_table();
-    return (int32_t)g_table.size();
+    return (int32_t)table().size();
 }
 
 const char *qlin_status_string(qlin_status s)
@@ -705,5 +713,20 @@ const char *qlin_status_string(qlin_status s)
 }
 
 int32_t qlin_abi_version(void) { return QLINEAR_ABI_VERSION; }
+
+int32_t qlin_stream_capture_id(void *stream, unsigned long long *capture_id)
+{
+    if (!capture_id)
+        return -1;
+    *capture_id = 0;
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    unsigned long long id = 0;
+    if (hipStreamGetCaptureInfo(static_cast<hipStream_t>(stream), &st, &id) != hipSuccess)
+        return -1;
+    if (st != hipStreamCaptureStatusActive)
+        return 0;
+    *capture_id = id;
+    return 1;
+}
 
 }  // extern "C"
