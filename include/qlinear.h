@@ -323,6 +323,33 @@ int32_t qlin_config_table_size(void);
 const char *qlin_status_string(qlin_status s);
 int32_t qlin_abi_version(void);
 
+/* scaled_mm / block_scaled_mm for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same validation, config selection, kernels and results as
+ * qlin_scaled_mm (scaling QLIN_TOKEN_CHANNEL, dtype e4m3 or int8) and
+ * qlin_block_scaled_mm (scaling QLIN_BLOCK128, dtype e4m3), with the split-K
+ * workspace taken from a 32 MiB device array inside the library instead of
+ * a caller's buffer.  Arguments as in those calls; the caller owns A, the
+ * scales, B and Y.
+ *  - The array is one per GPU, set up by the first call that needs it on that
+ *    GPU (its device address looked up once; its counter region cleared by a
+ *    small kernel on the caller's stream, recorded into the graph when that
+ *    first call is being captured) and held until the process ends.
+ *  - Nothing is allocated or freed, on the host or the device, on any call.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's partials: calls that may overlap in time on one GPU (different
+ *    streams, or graphs replayed concurrently) race on it and must not be
+ *    issued; calls ordered on one stream are safe.
+ *  - QLIN_ERR_WORKSPACE when the selected config needs more than the array
+ *    holds (32 MiB less 128 KiB of counters for the split partials
+ *    split_k * M * N * 4 bytes: never at M <= 256 on the tuned shapes); no
+ *    launch then.  QLIN_ERR_HIP when the device address cannot be obtained.
+ *    Other errors as in qlin_scaled_mm. */
+qlin_status qlin_scaled_mm_noalloc(qlin_scaling scaling, qlin_dtype dtype, int64_t M, int64_t N,
+                                   int64_t K, const void *A, int64_t lda, const float *a_scale,
+                                   const void *B, int64_t ldb, const float *b_scale, void *Y,
+                                   int64_t ldy, void *stream);
+
 /* Stream-capture state of `stream` (a hipStream_t; NULL is the null stream),
  * for callers that keep one split-K workspace per HIP graph: returns 1 and
  * sets *capture_id to the id of the capture in progress (unique per capture

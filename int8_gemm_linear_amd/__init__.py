@@ -131,6 +131,8 @@ def _lib():
     lib.qlin_status_string.restype = ctypes.c_char_p
     lib.qlin_abi_version.argtypes = []
     lib.qlin_abi_version.restype = ctypes.c_int32
+    lib.qlin_scaled_mm_noalloc.argtypes = [I, I, I64, I64, I64, P, I64, P, P, I64, P, P, I64, P]
+    lib.qlin_scaled_mm_noalloc.restype = I
     lib.qlin_stream_capture_id.argtypes = [P, ctypes.POINTER(ctypes.c_ulonglong)]
     lib.qlin_stream_capture_id.restype = ctypes.c_int32
     lib.qlin_quant_per_token.argtypes = [I, I64, I64, P, I64, P, I64, P, P]
@@ -456,6 +458,38 @@ def block_scaled_mm(a_q, a_scale, b_q, b_scale, out=None, config: Config | None 
         _call(_lib().qlin_block_scaled_mm, args, "qlin_block_scaled_mm")
     else:
         _call(_lib().qlin_block_scaled_mm_cfg, args + [ctypes.byref(c)], "qlin_block_scaled_mm_cfg")
+    return out
+
+
+def scaled_mm_noalloc(a_q, a_scale, b_q, b_scale, out, block: bool = False):
+    """scaled_mm (block=False) or block_scaled_mm (block=True) through the
+    library's allocation-free entry point: the split-K workspace is the
+    library's own per-GPU device array, and `out` must be given (nothing is
+    allocated).  Calls that overlap in time on one GPU must not be issued."""
+    dt = _dt(a_q)
+    if b_q.dtype != a_q.dtype:
+        raise TypeError("A and B must have the same dtype")
+    if block and dt != E4M3:
+        raise TypeError("block scaling takes float8_e4m3fn operands")
+    lda, ldb = _rows(a_q, "a_q"), _rows(b_q, "b_q")
+    M, K = a_q.shape
+    N = b_q.shape[0]
+    if b_q.shape[1] != K:
+        raise ValueError("A is [M,K] and B must be [N,K]")
+    if block:
+        _scale(a_scale, (M, K // 128), "a_scale")
+        _scale(b_scale, (N // 128, K // 128), "b_scale")
+    else:
+        _scale(a_scale, (M,), "a_scale")
+        _scale(b_scale, (N,), "b_scale")
+    if out is None or out.dtype != torch.bfloat16 or out.dim() != 2 or out.stride(1) != 1 or \
+            tuple(out.shape) != (M, N):
+        raise ValueError("out must be a bf16 [M,N] tensor with contiguous rows")
+    stream = torch.cuda.current_stream(a_q.device)
+    _call(_lib().qlin_scaled_mm_noalloc,
+          [BLOCK128 if block else TOKEN_CHANNEL, dt, M, N, K, a_q.data_ptr(), lda, a_scale.data_ptr(),
+           b_q.data_ptr(), ldb, b_scale.data_ptr(), out.data_ptr(), out.stride(0), stream.cuda_stream],
+          "qlin_scaled_mm_noalloc")
     return out
 
 

@@ -21,6 +21,7 @@ TABLE = os.path.join(PKG, "configs", "qlin_mi355x.cfg")
 
 SOURCES = [
     "qlin_api.cpp",
+    "qlin_noalloc.hip",
     "qlin_reduce.hip",
     "qlin_quant.hip",
     "qlin_fused.hip",

@@ -506,6 +506,30 @@ int fmt_of(qlin_dtype dt) { return dt == QLIN_INT8 ? FMT_INT8 : (dt == QLIN_E4M3
 
 }  // namespace
 
+namespace qlin {
+
+qlin_status run_problem(const Problem &pb, const qlin_config *cfg) { return run(pb, cfg); }
+
+qlin_status check_problem(const Problem &pb) { return validate(pb); }
+
+Problem problem(int fmt, int scal, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                const float *sA, const void *B, int64_t ldb, const float *sB, void *Y,
+                int64_t ldy, void *ws, size_t ws_bytes, void *stream)
+{
+    return make_problem(fmt, scal, M, N, K, A, lda, sA, B, ldb, sB, Y, ldy, ws, ws_bytes, stream);
+}
+
+size_t selected_workspace_bytes(int fmt, int scal, int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0)
+        return 0;
+    return ws_bytes(select_config(fmt, scal, M, N, K), M, N);
+}
+
+size_t counter_bytes() { return kCounterBytes; }
+
+}  // namespace qlin
+
 extern "C" {
 
 qlin_status qlin_scaled_mm_cfg(qlin_dtype dt, int64_t M, int64_t N, int64_t K, const void *A,

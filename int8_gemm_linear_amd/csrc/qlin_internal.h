@@ -93,4 +93,16 @@ const Instance *tile_h_instances_int8(int *count);
 // Split-K two-pass reduction + epilogue.
 hipError_t launch_reduce(int fmt, int scal, const KArgs &a, hipStream_t s);
 
+// The host dispatcher (qlin_api.cpp), for entry points in other units:
+// validate, select (or check) the config and launch; validate only; build a Problem; the
+// workspace bytes the selected config needs; the size of the counter region
+// at the start of every workspace.
+qlin_status run_problem(const Problem &pb, const qlin_config *cfg);
+qlin_status check_problem(const Problem &pb);   // argument checks only, no HIP call
+Problem problem(int fmt, int scal, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                const float *sA, const void *B, int64_t ldb, const float *sB, void *Y,
+                int64_t ldy, void *ws, size_t ws_bytes, void *stream);
+size_t selected_workspace_bytes(int fmt, int scal, int64_t M, int64_t N, int64_t K);
+size_t counter_bytes();
+
 }  // namespace qlin

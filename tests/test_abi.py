@@ -343,3 +343,19 @@ def test_grouped_default_config_is_valid_and_unsplit():
                 # (token/channel formats), the LDS-ring kernel below that K
                 if mr <= 3 and fmt != "block_fp8":
                     assert c.kernel == (q.KERNEL_GEMV if K >= 2048 else q.KERNEL_STREAM_LDS), (fmt, mr, K, c)
+
+
+def test_noalloc_validation_and_workspace_limit():
+    lib = q.lib()
+    # the scratch-array entry point validates like qlin_scaled_mm, before any HIP call
+    args = lambda sc, dt, M, N, K, A=A16, sA=S4, B=B16, sB=S4, Y=Y16: [
+        sc, dt, M, N, K, A, K, sA, B, K, sB, Y, N, None]
+    assert lib.qlin_scaled_mm_noalloc(*args(5, q.E4M3, 16, 256, 1024)) == ST["arg"]
+    assert lib.qlin_scaled_mm_noalloc(*args(q.BLOCK128, q.INT8, 16, 256, 1024)) == ST["arg"]
+    assert lib.qlin_scaled_mm_noalloc(*args(q.TOKEN_CHANNEL, q.INT8, 16, 256, 1000)) == ST["shape"]
+    assert lib.qlin_scaled_mm_noalloc(*args(q.TOKEN_CHANNEL, q.INT8, 16, 256, 1024, A=None)) == ST["null"]
+    assert lib.qlin_scaled_mm_noalloc(*args(q.BLOCK128, q.E4M3, 16, 200, 1024)) == ST["shape"]
+    assert lib.qlin_scaled_mm_noalloc(*args(q.TOKEN_CHANNEL, q.E4M3, 0, 256, 1024)) == ST["ok"]
+    # a config whose split partials exceed the 32 MiB array: rejected, nothing launched
+    assert q.workspace_size("block_fp8", 2048, 5120, 25600) > 32 << 20
+    assert lib.qlin_scaled_mm_noalloc(*args(q.BLOCK128, q.E4M3, 2048, 5120, 25600)) == ST["ws"]
