@@ -101,8 +101,7 @@ typedef enum qlin_kernel {
     QLIN_KERNEL_STREAM = 0,     /* weights streamed HBM -> registers; small M */
     QLIN_KERNEL_TILE = 1,       /* A and B tiles staged through a double-buffered LDS ring; large M */
     QLIN_KERNEL_STREAM_LDS = 2, /* weights and tokens copied HBM -> LDS in 1 KB row segments
-                                   through a multi-stage ring; small M; K % 256 == 0;
-                                   token/channel scaling only */
+                                   through a multi-stage ring; small M; K % 256 == 0 */
     QLIN_KERNEL_GEMV = 3        /* one wave per weight row, dot products on the vector ALUs;
                                    1-8 tokens (token/channel scaling) or 1-2 tokens
                                    (block scaling); split_k = 1 */

@@ -35,6 +35,7 @@ SOURCES = [
     "qlin_tile_block.hip",
     "qlin_stream_lds_fp8.hip",
     "qlin_stream_lds_int8.hip",
+    "qlin_stream_lds_block.hip",
     "qlin_gemv.hip",
 ]
 

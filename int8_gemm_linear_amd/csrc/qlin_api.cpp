@@ -55,7 +55,7 @@ const std::vector<Instance> &registry()
         const Instance *(*fns[])(int *) = {
             stream_instances_fp8, stream_instances_int8, stream_instances_block,
             tile_instances_fp8, tile_instances_int8, tile_instances_block,
-            stream_lds_instances_fp8, stream_lds_instances_int8,
+            stream_lds_instances_fp8, stream_lds_instances_int8, stream_lds_instances_block,
             tile_h_instances_fp8, tile_h_instances_int8, gemv_instances,
         };
         for (auto f : fns) {

@@ -112,6 +112,18 @@ __device__ inline void lds_dma16(const void *g, const void *lds)
                  : "memory", "m0");
 }
 
+// Copy 4 bytes per lane HBM/L2 -> LDS (global_load_lds_dword): lane i's
+// bytes land at lds + 4*i.  Same contract as lds_dma16 (inline assembly, no
+// register output, the caller counts its own copies in vmcnt).
+__device__ inline void lds_dma4(const void *g, const void *lds)
+{
+    const unsigned off = (unsigned)(size_t)lds;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(off))
+                 : "memory", "m0");
+}
+
 __device__ inline v4i ld_nt(const uint8_t *p)
 {
     return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));

@@ -38,7 +38,17 @@
 // Swap-AB orientation, Split-K partials / last arriver) is the stream
 // kernel's.  Variants and split-K as in the "Kernel Implementation" section
 // of "Building a High-Performance and Portable vLLM Linear Backend with
-// Helion"; token/channel scaling only (Block_FP8 uses the other kernels).
+// Helion".
+//
+// Block_FP8 (1x128 activation groups, 128x128 weight blocks, same page,
+// section "Helion Linear Backend / Scope"): a 128-byte K step is exactly one
+// K group, because chunks start on 256-byte boundaries.  Each step's product
+// goes to the matrix cores with a zero accumulator and is then added to the
+// running sum times sA[t, g] * sB[n / 128, g].  The chunk's group scales
+// travel with the chunk: every wave issues LS more copies per chunk
+// (global_load_lds_dword, 4 bytes per lane) that bring sA[m0 .. m0+TMS-1]
+// [chunk's groups] and sB[two weight-block rows][chunk's groups] into an
+// area after the stage's rows, so the chunk waits stay exact counts.
 #pragma once
 
 #include "qlin_device.h"
@@ -55,7 +65,7 @@ __device__ inline void wait_vm()
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int FMT, bool SWAP, int TMS, int TRW, int NW, int S, int CHK>
+template <int FMT, int SCAL, bool SWAP, int TMS, int TRW, int NW, int S, int CHK>
 __global__ void __launch_bounds__(64 * NW)
 k_stream_lds(KArgs p_)
 {
@@ -70,11 +80,20 @@ k_stream_lds(KArgs p_)
     constexpr int ROWS0 = TR + TMS;
     constexpr int INSTR = ((ROWS0 + RPI * NW - 1) / (RPI * NW)) * NW;   // padded
     constexpr int ROWS = INSTR * RPI;
-    constexpr int STAGE = ROWS * CHK;
-    constexpr int L = INSTR / NW;                    // per wave per chunk
+    constexpr int ROWB = ROWS * CHK;                 // the stage's rows
+    constexpr int L0 = INSTR / NW;                   // row copies per wave per chunk
+    // Block scaling: group scales of the chunk after the rows, as dwords
+    // [TMS][GPC] of sA then [2][GPC] of sB; LS dword copies per wave.
+    constexpr bool BLK = SCAL == SC_BLOCK;
+    constexpr int GPC = CHK / 128;                   // K groups per chunk
+    constexpr int SDW = BLK ? TMS * GPC + 2 * GPC : 0;
+    constexpr int LS = BLK ? (SDW + 64 * NW - 1) / (64 * NW) : 0;
+    constexpr int STAGE = ROWB + LS * NW * 256;
+    constexpr int L = L0 + LS;                       // copies per wave per chunk
     static_assert(CHK == 512 || CHK == 1024, "chunk");
     static_assert(TMS >= 1 && TMS <= 32, "tokens per tile");
     static_assert(S >= 1 && S <= 4 && L * (S - 1) <= 63, "ring");
+    static_assert(!BLK || FMT == FMT_E4M3, "block scaling is e4m3 only");
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[S * STAGE];
 
@@ -84,7 +103,7 @@ k_stream_lds(KArgs p_)
     const int g = lane >> 4;
 
     KArgs p = p_;
-    if (p.group_off && !enter_group<SC_TC>(p))
+    if (p.group_off && !enter_group<SCAL>(p))
         return;
     const int n0 = blockIdx.x * TR;
     const int m0 = blockIdx.y * TMS;
@@ -103,9 +122,9 @@ k_stream_lds(KArgs p_)
     // feed only outputs that are never stored), still issue their instruction
     // -- keeping the per-wave load count exact for the vmcnt waits -- but all
     // lanes read the same 16 bytes: one cache line instead of a 1 KB segment.
-    const uint8_t *src[L];
+    const uint8_t *src[L0];
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
+    for (int i = 0; i < L0; ++i) {
         const int ins = wave + i * NW;
         const int j = ins * RPI + (RPI == 2 ? (lane >> 5) : 0);       // stage row
         const int slot = RPI == 2 ? (lane & 31) : lane;
@@ -117,16 +136,54 @@ k_stream_lds(KArgs p_)
         src[i] = valid ? base + 16 * (slot ^ (j & 15)) : base;
     }
 
+    // Block scaling: per scale copy, the source of this lane's dword for the
+    // split's first chunk (chunk c adds c * GPC), its group within the chunk,
+    // or -1 for a lane with nothing to fetch (it reads a fixed, valid scale).
+    const float *ssrc[LS > 0 ? LS : 1];
+    int sgl[LS > 0 ? LS : 1];
+    const float *ssafe = BLK ? p.sA + (int64_t)m0 * p.G : nullptr;
+    if constexpr (BLK) {
+        const int g0 = kbeg >> 7;
+#pragma unroll
+        for (int i = 0; i < LS; ++i) {
+            const int idx = (wave + i * NW) * 64 + lane;
+            ssrc[i] = ssafe;
+            sgl[i] = -1;
+            if (idx < TMS * GPC) {
+                const int tok = idx / GPC, gl = idx % GPC;
+                if (m0 + tok < p.M) {
+                    ssrc[i] = p.sA + (int64_t)(m0 + tok) * p.G + g0 + gl;
+                    sgl[i] = gl;
+                }
+            } else if (idx < SDW) {
+                const int b = (idx - TMS * GPC) / GPC, gl = (idx - TMS * GPC) % GPC;
+                const int nb = (n0 >> 7) + b;
+                if (nb < (p.N >> 7)) {
+                    ssrc[i] = p.sB + (int64_t)nb * p.G + g0 + gl;
+                    sgl[i] = gl;
+                }
+            }
+        }
+    }
+
     auto issue = [&](int c) {
         const int k0 = kbeg + c * CHK;
         const int len = min(CHK, kend - k0);
         uint8_t *st = lds + (c % S) * STAGE;
         const int slot = RPI == 2 ? (lane & 31) : lane;
 #pragma unroll
-        for (int i = 0; i < L; ++i) {
+        for (int i = 0; i < L0; ++i) {
             const int ins = wave + i * NW;
             if (slot * 16 < len)
                 lds_dma16(src[i] + k0, st + ins * 1024);
+        }
+        if constexpr (BLK) {
+            const int glen = len >> 7;                 // groups in this chunk
+#pragma unroll
+            for (int i = 0; i < LS; ++i) {
+                const bool ok = sgl[i] >= 0 && sgl[i] < glen;
+                lds_dma4(ok ? ssrc[i] + c * GPC : ssafe, st + ROWB + (wave + i * NW) * 256);
+            }
         }
     };
 
@@ -144,7 +201,7 @@ k_stream_lds(KArgs p_)
     //   standard: sa4[tb] = sA[t..t+3], sb1[rb] = sB[n]
     float sa1[TB], sb1[RB];
     v4f sa4[TB], sb4[RB];
-    const bool scaled = p.acc_out == nullptr;
+    const bool scaled = !BLK && p.acc_out == nullptr;   // Block_FP8 sums arrive scaled
     if (scaled) {
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
@@ -183,6 +240,19 @@ k_stream_lds(KArgs p_)
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
         arow[tb] = TR + (tb * 16 + r16 < TMS ? tb * 16 + r16 : 0);
+    // Block scaling: where this lane's token scales and each 16-row block's
+    // weight scales sit in the stage's scale area (dword index of group 0).
+    int sa_at[TB][SWAP ? 1 : 4], sb_at[RB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int v = 0; v < (SWAP ? 1 : 4); ++v) {
+            const int tok = SWAP ? tb * 16 + r16 : tb * 16 + 4 * g + v;
+            sa_at[tb][v] = (tok < TMS ? tok : 0) * GPC;
+        }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+        sb_at[rb] = TMS * GPC + (((n0 + rb * 16) >> 7) - (n0 >> 7)) * GPC;
 
     for (int c = 0; c < nch; ++c) {
         const int after = min(S - 1, nch - 1 - c);   // chunks issued after c
@@ -213,12 +283,37 @@ k_stream_lds(KArgs p_)
                     af[tb][h] = *reinterpret_cast<const v4i *>(st + arow[tb] * CHK +
                                                                 16 * (piece ^ (arow[tb] & 15)));
             }
+            if constexpr (BLK) {
+                // one K group: product on the matrix cores, then promoted
+                const float *sc = reinterpret_cast<const float *>(st + ROWB);
+                float fb[RB];
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
+                for (int rb = 0; rb < RB; ++rb)
+                    fb[rb] = sc[sb_at[rb] + s];
 #pragma unroll
-                for (int tb = 0; tb < TB; ++tb)
-                    acc[rb][tb] = SWAP ? mma16<FMT>(bf[rb][0], bf[rb][1], af[tb][0], af[tb][1], acc[rb][tb])
-                                       : mma16<FMT>(af[tb][0], af[tb][1], bf[rb][0], bf[rb][1], acc[rb][tb]);
+                for (int tb = 0; tb < TB; ++tb) {
+                    v4f fa;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        fa[v] = sc[sa_at[tb][SWAP ? 0 : v] + s];
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        const A4 z = A4{0, 0, 0, 0};
+                        const A4 pr = SWAP ? mma16<FMT>(bf[rb][0], bf[rb][1], af[tb][0], af[tb][1], z)
+                                           : mma16<FMT>(af[tb][0], af[tb][1], bf[rb][0], bf[rb][1], z);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            acc[rb][tb][v] += pr[v] * (fa[v] * fb[rb]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int tb = 0; tb < TB; ++tb)
+                        acc[rb][tb] = SWAP ? mma16<FMT>(bf[rb][0], bf[rb][1], af[tb][0], af[tb][1], acc[rb][tb])
+                                           : mma16<FMT>(af[tb][0], af[tb][1], bf[rb][0], bf[rb][1], acc[rb][tb]);
+            }
         }
         if (c + S < nch) {
             __syncthreads();                     // every wave is done with stage c % S
@@ -276,12 +371,12 @@ k_stream_lds(KArgs p_)
                         continue;
                     if (!scaled) {
                         if (n + 3 < nend) {
-                            store_final4<FMT, SC_TC>(p, t, n, val[rb][tb]);
+                            store_final4<FMT, SCAL>(p, t, n, val[rb][tb]);
                         } else {
 #pragma unroll
                             for (int v = 0; v < 4; ++v)
                                 if (n + v < nend)
-                                    store_final<FMT, SC_TC>(p, t, n + v, val[rb][tb][v]);
+                                    store_final<FMT, SCAL>(p, t, n + v, val[rb][tb][v]);
                         }
                     } else if (n + 3 < nend) {
                         store_final4_pre<FMT, SC_TC>(p, t, n, val[rb][tb], sa1[tb], sb4[rb]);
@@ -302,7 +397,7 @@ k_stream_lds(KArgs p_)
                         if (t >= mend)
                             continue;
                         if (!scaled)
-                            store_final<FMT, SC_TC>(p, t, n, val[rb][tb][v]);
+                            store_final<FMT, SCAL>(p, t, n, val[rb][tb][v]);
                         else
                             p.Y[(int64_t)t * p.ldy + n] =
                                 bf16_bits(((float)val[rb][tb][v] * sa4[tb][v]) * sb1[rb]);
@@ -339,7 +434,7 @@ k_stream_lds(KArgs p_)
                     if (t >= mend || n >= nend)
                         continue;
                     if (!scaled)
-                        store_final<FMT, SC_TC>(p, t, n, sum);
+                        store_final<FMT, SCAL>(p, t, n, sum);
                     else
                         p.Y[(int64_t)t * p.ldy + n] =
                             bf16_bits(((float)sum * (SWAP ? sa1[tb] : sa4[tb][v])) *
@@ -398,16 +493,21 @@ k_stream_lds(KArgs p_)
     rearm(p.counters + tile);
 }
 
-template <int FMT, bool SWAP, int TMS, int TRW, int NW, int S, int CHK>
+template <int FMT, int SCAL, bool SWAP, int TMS, int TRW, int NW, int S, int CHK>
 hipError_t launch_stream_lds(const KArgs &a, dim3 grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_stream_lds<FMT, SWAP, TMS, TRW, NW, S, CHK>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((k_stream_lds<FMT, SCAL, SWAP, TMS, TRW, NW, S, CHK>), grid, dim3(64 * NW), 0,
+                       s, a);
     return hipGetLastError();
 }
 
 #define QLIN_STREAM_LDS_INSTANCE(FMT, BIT, SW, TMS, TRW, NW, S, CHK)                 \
     {{QLIN_KERNEL_STREAM_LDS, SW, TMS, TRW, CHK, 1, NW, S, 1, 0}, BIT, FMT, SC_TC, \
-     &launch_stream_lds<FMT, (SW) != 0, TMS, TRW, NW, S, CHK>}
+     &launch_stream_lds<FMT, SC_TC, (SW) != 0, TMS, TRW, NW, S, CHK>}
+
+#define QLIN_STREAM_LDS_INSTANCE_BLOCK(FMT, BIT, SW, TMS, TRW, NW, S, CHK)                \
+    {{QLIN_KERNEL_STREAM_LDS, SW, TMS, TRW, CHK, 1, NW, S, 1, 0}, BIT, FMT, SC_BLOCK, \
+     &launch_stream_lds<FMT, SC_BLOCK, (SW) != 0, TMS, TRW, NW, S, CHK>}
 
 // (weight rows, NW, S, CHK) per token count TMS; LDS per workgroup is about
 // S * (rows + TMS) * CHK bytes.  8-row tiles double the workgroup count for

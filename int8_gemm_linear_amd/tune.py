@@ -40,13 +40,20 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 COLD_BYTES = 512 << 20
 
 
-def candidates(fmt: str, M: int, N: int, K: int, max_split: int = 256):
-    """Every valid (instance, split_k, reduce) for the point."""
+def candidates(fmt: str, M: int, N: int, K: int, max_split: int = 256, kernels=None,
+               max_token_tiles: int = 4):
+    """Every valid (instance, split_k, reduce) for the point; `kernels`
+    restricts the kernel families, `max_token_tiles` the token tiles of the
+    stream kernels (ceil(M / tile_m))."""
     out = []
     KS = -(-K // 128)
     for base in q.instances_for(fmt):
-        if base.kernel in (q.KERNEL_STREAM, q.KERNEL_STREAM_LDS) and -(-M // base.tile_m) > 4:
+        if kernels is not None and base.kernel not in kernels:
+            continue
+        if base.kernel in (q.KERNEL_STREAM, q.KERNEL_STREAM_LDS) and -(-M // base.tile_m) > max_token_tiles:
             continue                      # the stream kernels are for small token counts
+        if base.kernel == q.KERNEL_STREAM_LDS and base.tile_m > 2 * M and base.tile_m > 4:
+            continue                      # a token tile mostly of padding
         if base.kernel == q.KERNEL_TILE and M < 16:
             continue
         if base.kernel == q.KERNEL_GEMV and M > base.tile_m:
@@ -133,11 +140,16 @@ def agree(fmt, y, ref) -> bool:
                 and (torch.linalg.vector_norm(yf - rf).item() <= 1e-2 * nrm or nrm == 0))
 
 
-def tune_point(fmt, M, N, K, log=None, done=None, max_cands=None, verbose=False):
+def tune_point(fmt, M, N, K, log=None, done=None, max_cands=None, verbose=False, **sel):
+    """Times every candidate of the point (`sel`: the filters of candidates());
+    the config the library selects now is always among them."""
     pt = Point(fmt, M, N, K)
-    cands = candidates(fmt, M, N, K)
+    cands = candidates(fmt, M, N, K, **sel)
     if max_cands:
         cands = cands[:max_cands]
+    cur = q.select_config(fmt, M, N, K)
+    if cur not in cands:
+        cands = [cur] + cands
     ref = pt.call(q.select_config(fmt, M, N, K), out=torch.empty_like(pt.y)).clone()
     torch.cuda.synchronize()
     results = []
@@ -183,7 +195,13 @@ def main():
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--min-m", type=int, default=0)
     ap.add_argument("--max-m", type=int, default=1 << 30)
+    ap.add_argument("--kernels", default=None, help="comma list of kernel families to sweep "
+                    "(0 stream, 1 tile, 2 LDS-ring stream, 3 GEMV); the current pick is always kept")
+    ap.add_argument("--max-split", type=int, default=256)
+    ap.add_argument("--max-token-tiles", type=int, default=4)
     args = ap.parse_args()
+    sel = {"max_split": args.max_split, "max_token_tiles": args.max_token_tiles,
+           "kernels": None if args.kernels is None else {int(k) for k in args.kernels.split(",")}}
     sys.path.insert(0, ROOT)
     import synth
 
@@ -207,7 +225,7 @@ def main():
     t0 = time.time()
     for (fmt, M, N, K) in points:
         res = tune_point(fmt, M, N, K, log=log, done=done, max_cands=args.max_cands,
-                         verbose=args.verbose)
+                         verbose=args.verbose, **sel)
         us, c, _ = res[0]
         dflt = q.select_config(fmt, M, N, K)
         dus = next((r[0] for r in res if r[1] == dflt), float("nan"))
