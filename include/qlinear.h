@@ -122,7 +122,11 @@ typedef enum qlin_reduce {
  * each wave loads per pipeline step (multiple of 128), waves_n x waves_k
  * waves split the tile's rows and the split's K range.  For STREAM_LDS:
  * tile_m / tile_n as for STREAM, tile_k = bytes per row per LDS chunk (512
- * or 1024), waves_k waves share each chunk's K steps, stages = ring depth.
+ * or 1024), waves_k waves share each chunk's K steps, stages = ring depth,
+ * waves_n = 1 for workgroups of tile_n weight rows each, or 2 for spread
+ * placement: N in 8-row units shared evenly over a grid that is a multiple
+ * of the device's compute units per (token tile, split), at most tile_n
+ * rows per workgroup.
  * For the TILE kernel:
  * tile_m x tile_n output tile, waves_n x waves_k is the wave grid over the
  * tile (rows x columns), stages = depth of the LDS ring; tile_k = 128 is the

@@ -63,9 +63,36 @@ const std::vector<Instance> &registry()
             const Instance *p = f(&n);
             r.insert(r.end(), p, p + n);
         }
+        // Every LDS-ring instance also runs with spread row placement
+        // (waves_n = 2): the same kernel, rows shared evenly over a grid
+        // sized to the CU count instead of one tile of tile_n rows each.
+        const size_t n = r.size();
+        for (size_t i = 0; i < n; ++i)
+            if (r[i].cfg.kernel == QLIN_KERNEL_STREAM_LDS) {
+                Instance twin = r[i];
+                twin.cfg.waves_n = 2;
+                r.push_back(twin);
+            }
         return r;
     }();
     return all;
+}
+
+// Compute units of the current device (256 on MI355X; also the answer when
+// no device is visible, so host-only queries stay deterministic).
+int cu_count()
+{
+    static std::atomic<int> cached{0};
+    int v = cached.load(std::memory_order_relaxed);
+    if (v > 0)
+        return v;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    cached.store(cus, std::memory_order_relaxed);
+    return cus;
 }
 
 bool same_shape(const qlin_config &a, const qlin_config &b)
@@ -183,15 +210,30 @@ int ilog2_exact(int v)
     return l;
 }
 
-// Stream kernel: grid (weight tiles, token tiles); tile kernel: one flat
+bool spread_rows(const qlin_config &c)
+{
+    return c.kernel == QLIN_KERNEL_STREAM_LDS && c.waves_n == 2;
+}
+
+// Stream kernels: grid (weight tiles, token tiles); tile kernel: one flat
 // dimension over all output tiles (remapped in-kernel for XCD locality).
-void grid_of(const qlin_config &c, int64_t M, int64_t N, int64_t *gx, int64_t *gy)
+// Spread placement (LDS-ring kernel): 8-row units over a grid.x that is a
+// multiple of the CUs left per (token tile, grid.z) slice, each workgroup
+// taking at most tile_n rows.  `z` is grid.z (split_k, or 1 for grouped
+// calls, whose grid.z holds the groups).
+void grid_of(const qlin_config &c, int64_t M, int64_t N, int64_t z, int64_t *gx, int64_t *gy)
 {
     const int64_t tn = (N + c.tile_n - 1) / c.tile_n;
     const int64_t tm = (M + c.tile_m - 1) / c.tile_m;
     if (c.kernel == QLIN_KERNEL_TILE) {
         *gx = tn * tm;
         *gy = 1;
+    } else if (spread_rows(c)) {
+        const int64_t units = (N + 7) / 8;
+        const int64_t need = (units + c.tile_n / 8 - 1) / (c.tile_n / 8);
+        const int64_t slots = std::max<int64_t>(1, cu_count() / (tm * std::max<int64_t>(1, z)));
+        *gx = std::min(units, (need + slots - 1) / slots * slots);
+        *gy = tm;
     } else {
         *gx = tn;
         *gy = tm;
@@ -239,7 +281,7 @@ qlin_config default_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
         c.stages = 2;
     }
     int64_t gx, gy;
-    grid_of(c, M, N, &gx, &gy);
+    grid_of(c, M, N, c.split_k, &gx, &gy);
     const int64_t kw = c.kernel == QLIN_KERNEL_STREAM ? c.waves_k : 1;
     // Split K until the grid covers the CUs (tiles: half of them; a tile's
     // workgroup holds a whole CU's LDS), keeping >= 8 K steps per split for
@@ -343,7 +385,7 @@ qlin_status check_config(int fmt, int scal, int64_t M, int64_t N, int64_t K,
     if (c.kernel == QLIN_KERNEL_GEMV && c.split_k != 1)
         return QLIN_ERR_BAD_CONFIG;   // a wave covers a weight row's whole K
     int64_t gx, gy;
-    grid_of(c, M, N, &gx, &gy);
+    grid_of(c, M, N, c.split_k, &gx, &gy);
     if (gx > 0x7fffffff || gy > 65535)
         return QLIN_ERR_BAD_CONFIG;
     if (c.split_k > 1 && c.reduce == QLIN_REDUCE_LAST_ARRIVER && gx * gy > kMaxCounters)
@@ -469,7 +511,9 @@ qlin_status run(const Problem &pb, const qlin_config *cfg_in)
         a.sb_gstride = pb.sb_gstride;
     }
     int64_t gx, gy;
-    grid_of(cfg, pb.M, pb.N, &gx, &gy);
+    grid_of(cfg, pb.M, pb.N, grouped ? 1 : cfg.split_k, &gx, &gy);
+    if (spread_rows(cfg))
+        a.nspread = (int)((pb.N + 7) / 8);
     const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)(grouped ? pb.groups : cfg.split_k));
     hipError_t e = inst->fn(a, grid, pb.stream);
     if (e == hipSuccess && cfg.split_k > 1 && cfg.reduce == QLIN_REDUCE_TWO_PASS)

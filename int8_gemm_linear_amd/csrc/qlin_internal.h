@@ -33,6 +33,8 @@ struct KArgs {
     int split_k;
     int steps_per_split; // 128-byte K steps per split
     int reduce;          // qlin_reduce
+    int nspread;         // STREAM_LDS spread placement: 8-row units (ceil(N/8)) shared
+                         // evenly over grid.x; 0 = tiles of tile_n rows
     // Grouped GEMM (mixture of experts): grid.z is the group; group g owns
     // rows group_off[g] .. group_off[g+1]-1 of A, sA and Y (at most M of
     // them) and the weights B + g * b_gstride bytes, sB + g * sb_gstride.

@@ -8,7 +8,7 @@
 // The LDS round trip costs nothing that matters here: LDS bandwidth is far
 // above a CU's share of HBM bandwidth.
 //
-// Workgroup: NW waves own TR = 8, 16, 32, 48 or 64 weight rows (the matrix core sees
+// Workgroup: NW waves own TR = 8, 16, 32, 48, 64, 96 or 128 weight rows (the matrix core sees
 // blocks of 16; with 8 rows, fragment rows 8..15 repeat rows 0..7 and their
 // outputs are dropped, which doubles the workgroup count for small N without
 // a split-K reduction) and TMS tokens (1..32; the
@@ -75,7 +75,8 @@ k_stream_lds(KArgs p_)
     constexpr int TR = TRW;                          // weight rows of the workgroup
     constexpr int RB = TR >= 16 ? TR / 16 : 1;       // 16-row matrix-core blocks
     constexpr int RMASK = TR >= 16 ? 15 : TR - 1;    // fragment row within the stage
-    static_assert(TR == 8 || TR == 16 || TR == 32 || TR == 48 || TR == 64, "weight rows");
+    static_assert(TR == 8 || TR == 16 || TR == 32 || TR == 48 || TR == 64 || TR == 96 || TR == 128,
+                  "weight rows");
     constexpr int RPI = 1024 / CHK;                  // rows per load instruction
     constexpr int ROWS0 = TR + TMS;
     constexpr int INSTR = ((ROWS0 + RPI * NW - 1) / (RPI * NW)) * NW;   // padded
@@ -105,7 +106,19 @@ k_stream_lds(KArgs p_)
     KArgs p = p_;
     if (p.group_off && !enter_group<SCAL>(p))
         return;
-    const int n0 = blockIdx.x * TR;
+    // Weight rows of the workgroup: TR rows per workgroup, or (spread
+    // placement) 8-row units shared evenly over grid.x, at most TR rows each,
+    // so a grid sized to the CU count gives every CU the same number of rows.
+    int n0, nend;
+    if (p.nspread) {
+        const int u0 = (int)((int64_t)p.nspread * blockIdx.x / gridDim.x);
+        const int u1 = (int)((int64_t)p.nspread * (blockIdx.x + 1) / gridDim.x);
+        n0 = 8 * u0;
+        nend = min(p.N, 8 * u1);
+    } else {
+        n0 = blockIdx.x * TR;
+        nend = min(p.N, n0 + TR);
+    }
     const int m0 = blockIdx.y * TMS;
     const int split = split_index(p);
     if (m0 >= p.M)
@@ -118,8 +131,9 @@ k_stream_lds(KArgs p_)
     const int kend = min(KP, split * pps + pps) * 256;
     const int nch = (kend - kbeg + CHK - 1) / CHK;
 
-    // Per-instruction source rows.  Padding rows, and rows past N or M (they
-    // feed only outputs that are never stored), still issue their instruction
+    // Per-instruction source rows.  Padding rows, and rows past the
+    // workgroup's weight rows or past M (they feed only outputs that are
+    // never stored), still issue their instruction
     // -- keeping the per-wave load count exact for the vmcnt waits -- but all
     // lanes read the same 16 bytes: one cache line instead of a 1 KB segment.
     const uint8_t *src[L0];
@@ -130,7 +144,7 @@ k_stream_lds(KArgs p_)
         const int slot = RPI == 2 ? (lane & 31) : lane;
         const bool isb = j < TR;
         const int row = isb ? n0 + j : m0 + j - TR;
-        const bool valid = isb ? row < p.N : (j < TR + TMS && row < p.M);
+        const bool valid = isb ? row < nend : (j < TR + TMS && row < p.M);
         const uint8_t *base = isb ? p.B + (int64_t)(valid ? row : 0) * p.ldb
                                   : p.A + (int64_t)(valid ? row : 0) * p.lda;
         src[i] = valid ? base + 16 * (slot ^ (j & 15)) : base;
@@ -242,7 +256,7 @@ k_stream_lds(KArgs p_)
         arow[tb] = TR + (tb * 16 + r16 < TMS ? tb * 16 + r16 : 0);
     // Block scaling: where this lane's token scales and each 16-row block's
     // weight scales sit in the stage's scale area (dword index of group 0).
-    int sa_at[TB][SWAP ? 1 : 4], sb_at[RB];
+    int sa_at[TB][SWAP ? 1 : 4], sb_at[RB];   // sb_at: this lane's weight row(s) of block rb
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
@@ -252,7 +266,7 @@ k_stream_lds(KArgs p_)
         }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
-        sb_at[rb] = TMS * GPC + (((n0 + rb * 16) >> 7) - (n0 >> 7)) * GPC;
+        sb_at[rb] = TMS * GPC + (((n0 + rb * 16 + (SWAP ? 4 * g : r16)) >> 7) - (n0 >> 7)) * GPC;
 
     for (int c = 0; c < nch; ++c) {
         const int after = min(S - 1, nch - 1 - c);   // chunks issued after c
@@ -358,7 +372,6 @@ k_stream_lds(KArgs p_)
     //   SWAP:     n = n0 + 16*rb + 4*g + v,  t = m0 + 16*tb + r16
     //   standard: n = n0 + 16*rb + r16,      t = m0 + 16*tb + 4*g + v
     const int mend = min(p.M, m0 + TMS);           // tokens of this tile
-    const int nend = min(p.N, n0 + TR);            // weight rows of this tile
     auto emit = [&](const A4 (&val)[RB][TB]) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -535,5 +548,13 @@ hipError_t launch_stream_lds(const KArgs &a, dim3 grid, hipStream_t s)
     X(FMT, BIT, SW, 32, 64, 8, 3, 512),            \
     X(FMT, BIT, SW, 16, 48, 8, 3, 512),            \
     X(FMT, BIT, SW, 32, 48, 8, 3, 512)
+
+// Wide tiles for 16-32 tokens: every workgroup copies its token rows once per
+// K range, so rows per workgroup set the token bytes per weight byte
+// (TMS / TR); split-K then keeps the grid wide.
+#define QLIN_STREAM_LDS_WIDE(X, FMT, BIT, SW)      \
+    X(FMT, BIT, SW, 16, 96, 8, 2, 512),            \
+    X(FMT, BIT, SW, 32, 96, 8, 2, 512),            \
+    X(FMT, BIT, SW, 16, 128, 8, 2, 512)
 
 }  // namespace qlin

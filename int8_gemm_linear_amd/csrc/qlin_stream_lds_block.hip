@@ -6,7 +6,9 @@ namespace qlin {
 
 static const Instance kInstances[] = {
     QLIN_STREAM_LDS_SHAPES(QLIN_STREAM_LDS_INSTANCE_BLOCK, FMT_E4M3, FB_BLOCK, 0),
-    QLIN_STREAM_LDS_SHAPES(QLIN_STREAM_LDS_INSTANCE_BLOCK, FMT_E4M3, FB_BLOCK, 1)};
+    QLIN_STREAM_LDS_SHAPES(QLIN_STREAM_LDS_INSTANCE_BLOCK, FMT_E4M3, FB_BLOCK, 1),
+    QLIN_STREAM_LDS_WIDE(QLIN_STREAM_LDS_INSTANCE_BLOCK, FMT_E4M3, FB_BLOCK, 0),
+    QLIN_STREAM_LDS_WIDE(QLIN_STREAM_LDS_INSTANCE_BLOCK, FMT_E4M3, FB_BLOCK, 1)};
 
 const Instance *stream_lds_instances_block(int *count)
 {

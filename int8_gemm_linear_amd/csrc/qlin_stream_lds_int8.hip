@@ -5,7 +5,9 @@ namespace qlin {
 
 static const Instance kInstances[] = {
     QLIN_STREAM_LDS_SHAPES(QLIN_STREAM_LDS_INSTANCE, FMT_INT8, FB_INT8, 0),
-    QLIN_STREAM_LDS_SHAPES(QLIN_STREAM_LDS_INSTANCE, FMT_INT8, FB_INT8, 1)};
+    QLIN_STREAM_LDS_SHAPES(QLIN_STREAM_LDS_INSTANCE, FMT_INT8, FB_INT8, 1),
+    QLIN_STREAM_LDS_WIDE(QLIN_STREAM_LDS_INSTANCE, FMT_INT8, FB_INT8, 0),
+    QLIN_STREAM_LDS_WIDE(QLIN_STREAM_LDS_INSTANCE, FMT_INT8, FB_INT8, 1)};
 
 const Instance *stream_lds_instances_int8(int *count)
 {

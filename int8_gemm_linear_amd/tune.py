@@ -199,6 +199,9 @@ def main():
                     "(0 stream, 1 tile, 2 LDS-ring stream, 3 GEMV); the current pick is always kept")
     ap.add_argument("--max-split", type=int, default=256)
     ap.add_argument("--max-token-tiles", type=int, default=4)
+    ap.add_argument("--min-gain", type=float, default=0.02,
+                    help="keep the current pick unless the best candidate is faster by this fraction "
+                         "(timings of one run differ by about that much between candidates of equal speed)")
     args = ap.parse_args()
     sel = {"max_split": args.max_split, "max_token_tiles": args.max_token_tiles,
            "kernels": None if args.kernels is None else {int(k) for k in args.kernels.split(",")}}
@@ -229,6 +232,8 @@ def main():
         us, c, _ = res[0]
         dflt = q.select_config(fmt, M, N, K)
         dus = next((r[0] for r in res if r[1] == dflt), float("nan"))
+        if dus == dus and us > dus * (1.0 - args.min_gain):
+            us, c = dus, dflt
         best[(fmt, M, N, K)] = c
         print(f"[tune] {fmt:9s} M={M:5d} N={N:6d} K={K:6d}: best {us:8.2f} us "
               f"({alg_bytes(fmt, M, N, K) / us / 1e6:.3f} TB/s, {2 * M * N * K / us / 1e6:.1f} TFLOP/s) "

@@ -286,3 +286,34 @@ def test_empty_inputs():
         b = torch.zeros((64, 128), dtype=torch.uint8, device="cuda").view(dt)
         y = q.scaled_mm(a, torch.ones(0, device="cuda"), b, torch.ones(64, device="cuda"))
         assert y.shape == (0, 64)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "fp8", "block_fp8"])
+def test_spread_row_placement(fmt):
+    # LDS-ring kernel with rows shared evenly over a grid sized to the CUs
+    # (waves_n = 2): workgroups start at any multiple of 8 rows, hold several
+    # 8-row units, and (Block_FP8) straddle 128-row weight blocks.  Every tile
+    # width, both orientations, with and without split-K.
+    for M, N, K in ((32, 5120, 1024), (16, 2944, 2048), (5, 1280, 512)):
+        case = small_case(fmt, M, N, K, root=24)
+        ref = small_ref(fmt, M, N, K, root=24)
+        dev = parity.to_device(case)
+        first = None
+        cfgs = {}
+        for c in q.instances_for(fmt):
+            if c.kernel == q.KERNEL_STREAM_LDS and c.waves_n == 2 and M <= c.tile_m <= 2 * max(M, 8):
+                cfgs.setdefault((c.tile_n, c.variant), c)
+        assert cfgs
+        for c in cfgs.values():
+            for split, red in ((1, 1), (2, q.REDUCE_LAST_ARRIVER), (2, q.REDUCE_TWO_PASS)):
+                cc = c.replace(split_k=split, reduce=red)
+                if q.check_config(fmt, M, N, K, cc) != 0:
+                    continue
+                say("spread", fmt, (M, N, K), cc)
+                y = call(case, dev, cc)
+                torch.cuda.synchronize()
+                parity.check_case(case, y, ref, what=f"{fmt} {cc}")
+                if fmt == "int8":
+                    yb = parity.y_bits(y)
+                    first = yb if first is None else first
+                    assert np.array_equal(yb, first), f"int8 disagreement at {cc}"
