@@ -36,8 +36,10 @@
 // columns to store.  Split-K is grid.z, as in the stream kernel.
 // Block_FP8 promotes each 128-wide K group into the running fp32 sum with
 // sA[t][g] * sB[n/128][g] (built with SWAP only, where each lane needs one
-// token scale per block and one weight-block scale per wave, and with S = 2:
-// the scales of step s+1 are loaded into registers next to its copy).
+// token scale per block and one weight-block scale per wave).  A step's
+// group scales travel with its stage: global_load_lds_dword copies (4 bytes
+// per lane) of sA[m0 .. m0+BM-1][g] and sB[n0/128 .. (n0+BN-1)/128][g] into
+// an area after the stage's rows, counted in the same exact waits.
 #pragma once
 
 #include "qlin_device.h"
@@ -400,11 +402,17 @@ k_tile(KArgs p_)
     constexpr int FM = WTM / 32;
     constexpr int FN = WTN / 32;
     constexpr int ROWS = BM + BN;
-    constexpr int STAGE = ROWS * 128;
+    constexpr int ROWB = ROWS * 128;                  // the stage's operand rows
+    // Block scaling: the step's scales after the rows, as dwords [BM] of sA
+    // then [BN/128] of sB; LSC dword copies per wave.
+    constexpr bool BLK = SCAL == SC_BLOCK;
+    constexpr int SDW = BLK ? BM + BN / 128 : 0;
+    constexpr int LSC = BLK ? (SDW + 64 * NW - 1) / (64 * NW) : 0;
+    constexpr int STAGE = ROWB + LSC * NW * 256;
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
     static_assert(ROWS % 8 == 0, "rows");
     static_assert(S >= 2 && S <= 6 && S * STAGE <= 160 * 1024, "stages");
-    static_assert(SCAL == SC_TC || S == 2, "block scaling keeps scales in a register double buffer");
+    static_assert(!BLK || (SWAP && BN % 128 == 0), "block scaling: Swap-AB, whole weight blocks");
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[S * STAGE];
 
@@ -450,8 +458,23 @@ k_tile(KArgs p_)
     }
 
     static_assert(ROWS / 8 % NW == 0, "copies must split evenly over the waves");
-    constexpr int L = GPW + (SCAL == SC_BLOCK ? FM + FN : 0);   // loads per wave per step
+    constexpr int L = GPW + LSC;                      // copies per wave per step
     static_assert(L * (S - 2) <= 63, "vmcnt range");
+
+    // Block scaling: source of this lane's scale dword at step 0 (step st adds
+    // st); rows past M and weight blocks past N read the last valid one.
+    const float *ssrc[LSC > 0 ? LSC : 1];
+    if constexpr (BLK) {
+#pragma unroll
+        for (int i = 0; i < LSC; ++i) {
+            const int idx = (wave + i * NW) * 64 + lane;
+            if (idx < BM)
+                ssrc[i] = p.sA + (int64_t)min(m0 + idx, p.M - 1) * p.G;
+            else
+                ssrc[i] = p.sB + (int64_t)min((n0 >> 7) + min(idx - BM, BN / 128 - 1),
+                                              (p.N >> 7) - 1) * p.G;
+        }
+    }
 
     auto issue = [&](int st, int stage) {
         uint8_t *dst0 = lds + stage * STAGE;
@@ -461,22 +484,10 @@ k_tile(KArgs p_)
             if (GROUPS % NW == 0 || grp_i < GROUPS)
                 lds_dma16(src[i] + (int64_t)st * 128, dst0 + grp_i * 1024);
         }
-    };
-
-    // Block_FP8 scales of a step, prefetched with the stage copy.
-    float sa_next[FM], sb_next[FN];
-    auto load_scales = [&](int st) {
-        if constexpr (SCAL == SC_BLOCK) {
+        if constexpr (BLK) {
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int t = min(m0 + wm * WTM + fm * 32 + (lane & 31), p.M - 1);
-                sa_next[fm] = p.sA[(int64_t)t * p.G + st];
-            }
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const int nbk = min(n0 + wn * WTN + fn * 32, p.N - 1) >> 7;
-                sb_next[fn] = p.sB[(int64_t)nbk * p.G + st];
-            }
+            for (int i = 0; i < LSC; ++i)
+                lds_dma4(ssrc[i] + st, dst0 + ROWB + (wave + i * NW) * 256);
         }
     };
 
@@ -493,26 +504,24 @@ k_tile(KArgs p_)
     const int fh = lane >> 5;          // 64-byte half of the K step
 
     const int nst = s_end - s_beg;
-    for (int i = 0; i < S - 1 && i < nst; ++i) {
+    for (int i = 0; i < S - 1 && i < nst; ++i)
         issue(s_beg + i, i);
-        load_scales(s_beg + i);
-    }
     for (int i = 0; i < nst; ++i) {
         const int s = s_beg + i;
-        float sa[FM], sb[FN];
-        if constexpr (SCAL == SC_BLOCK) {
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) sa[fm] = sa_next[fm];
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) sb[fn] = sb_next[fn];
-        }
         wait_steps<L, S - 2>(nst - 1 - i);              // steps issued after step i stay in flight
         __syncthreads();
-        if (i + S - 1 < nst) {
+        if (i + S - 1 < nst)
             issue(s + S - 1, (i + S - 1) % S);
-            load_scales(s + S - 1);
-        }
         const uint8_t *la = lds + (i % S) * STAGE;
+        float sa[FM], sb[FN];
+        if constexpr (BLK) {
+            const float *sc = reinterpret_cast<const float *>(la + ROWB);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) sa[fm] = sc[wm * WTM + fm * 32 + fr];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                sb[fn] = sc[BM + ((n0 + wn * WTN + fn * 32) >> 7) - (n0 >> 7)];
+        }
         const uint8_t *lb = la + BM * 128;
         v4i bf[FN][4];
 #pragma unroll
@@ -659,6 +668,8 @@ hipError_t launch_tile(const KArgs &a, dim3 grid, hipStream_t s)
 // (BM, BN, WM, WN, S) for token/channel scaling; LDS = S * (BM + BN) * 128 B.
 #define QLIN_TILE_SHAPES(X, FMT, SCAL, BIT, SW) \
     X(FMT, SCAL, BIT, SW, 64, 128, 1, 4, 4),    \
+    X(FMT, SCAL, BIT, SW, 64, 128, 2, 4, 4),    \
+    X(FMT, SCAL, BIT, SW, 64, 128, 2, 4, 6),    \
     X(FMT, SCAL, BIT, SW, 128, 128, 2, 2, 2),   \
     X(FMT, SCAL, BIT, SW, 128, 128, 2, 2, 4),   \
     X(FMT, SCAL, BIT, SW, 128, 128, 4, 2, 4),   \
@@ -670,16 +681,23 @@ hipError_t launch_tile(const KArgs &a, dim3 grid, hipStream_t s)
     X(FMT, SCAL, BIT, SW, 256, 128, 4, 2, 3),   \
     X(FMT, SCAL, BIT, SW, 128, 256, 2, 4, 3)
 
-// Block scaling: S = 2.
+// Block scaling (the stage also carries the step's scales, under 2 KB).
 #define QLIN_TILE_SHAPES_BLOCK(X, FMT, SCAL, BIT, SW) \
     X(FMT, SCAL, BIT, SW, 64, 128, 1, 4, 2),          \
+    X(FMT, SCAL, BIT, SW, 64, 128, 1, 4, 4),          \
+    X(FMT, SCAL, BIT, SW, 64, 128, 2, 4, 4),          \
+    X(FMT, SCAL, BIT, SW, 64, 128, 2, 4, 5),          \
     X(FMT, SCAL, BIT, SW, 128, 128, 2, 2, 2),         \
+    X(FMT, SCAL, BIT, SW, 128, 128, 2, 2, 4),         \
     X(FMT, SCAL, BIT, SW, 128, 128, 4, 2, 2),         \
+    X(FMT, SCAL, BIT, SW, 128, 128, 4, 2, 4),         \
     X(FMT, SCAL, BIT, SW, 128, 256, 2, 2, 2),         \
     X(FMT, SCAL, BIT, SW, 256, 128, 2, 2, 2),         \
     X(FMT, SCAL, BIT, SW, 256, 256, 2, 4, 2),         \
     X(FMT, SCAL, BIT, SW, 256, 256, 4, 2, 2),         \
     X(FMT, SCAL, BIT, SW, 256, 128, 4, 2, 2),         \
-    X(FMT, SCAL, BIT, SW, 128, 256, 2, 4, 2)
+    X(FMT, SCAL, BIT, SW, 256, 128, 4, 2, 3),         \
+    X(FMT, SCAL, BIT, SW, 128, 256, 2, 4, 2),         \
+    X(FMT, SCAL, BIT, SW, 128, 256, 2, 4, 3)
 
 }  // namespace qlin

@@ -357,5 +357,18 @@ def test_noalloc_validation_and_workspace_limit():
     assert lib.qlin_scaled_mm_noalloc(*args(q.BLOCK128, q.E4M3, 16, 200, 1024)) == ST["shape"]
     assert lib.qlin_scaled_mm_noalloc(*args(q.TOKEN_CHANNEL, q.E4M3, 0, 256, 1024)) == ST["ok"]
     # a config whose split partials exceed the 32 MiB array: rejected, nothing launched
-    assert q.workspace_size("block_fp8", 2048, 5120, 25600) > 32 << 20
-    assert lib.qlin_scaled_mm_noalloc(*args(q.BLOCK128, q.E4M3, 2048, 5120, 25600)) == ST["ws"]
+    fmt, M, N, K = oversize_shape()
+    sc, dt = q.FORMATS[fmt]
+    assert lib.qlin_scaled_mm_noalloc(*args(sc, dt, M, N, K)) == ST["ws"]
+
+
+OVERSIZE = [("block_fp8", 2048, 5120, 25600), ("block_fp8", 512, 4096, 12288),
+            ("fp8", 1024, 4096, 12288), ("int8", 2048, 5120, 25600), ("fp8", 2048, 5120, 25600)]
+
+
+def oversize_shape():
+    """A shape whose selected config needs more than the 32 MiB scratch array."""
+    for fmt, M, N, K in OVERSIZE:
+        if q.workspace_size(fmt, M, N, K) > 32 << 20:
+            return fmt, M, N, K
+    raise AssertionError("no candidate shape needs more than 32 MiB of split-K workspace")

@@ -99,14 +99,15 @@ def test_noalloc_graph_replay():
 
 
 def test_noalloc_too_large_workspace_is_rejected():
-    # Block_FP8 at M = 2048 on (25600, 5120) splits in two: 84 MB of partials
-    fmt, M, N, K = "block_fp8", 2048, 5120, 25600
-    assert q.workspace_size(fmt, M, N, K) > 32 << 20
-    a = torch.zeros((M, K), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
-    b = torch.zeros((N, K), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
-    sa = torch.ones((M, K // 128), device="cuda")
-    sb = torch.ones((N // 128, K // 128), device="cuda")
+    from tests.test_abi import oversize_shape
+    fmt, M, N, K = oversize_shape()
+    block = fmt == "block_fp8"
+    dt = torch.int8 if fmt == "int8" else torch.float8_e4m3fn
+    a = torch.zeros((M, K), dtype=torch.uint8, device="cuda").view(dt)
+    b = torch.zeros((N, K), dtype=torch.uint8, device="cuda").view(dt)
+    sa = torch.ones((M, K // 128) if block else (M,), device="cuda")
+    sb = torch.ones((N // 128, K // 128) if block else (N,), device="cuda")
     out = nan_out(M, N)
     with pytest.raises(q.QlinError) as e:
-        q.scaled_mm_noalloc(a, sa, b, sb, out=out, block=True)
+        q.scaled_mm_noalloc(a, sa, b, sb, out=out, block=block)
     assert e.value.status == 5
