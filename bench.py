@@ -333,13 +333,6 @@ def producer_points(reps: int = 8, target_bytes: int = 1 << 30):
             "copies (~1 GiB between reuses), hipEvents", "points": out}
 
 
-# Mixture-of-experts layers of a 30B-class model with 3B active parameters
-# (hidden 2048, 128 experts, 8 per token, expert width 768): gate_up
-# (K=2048, N=1536) and down (K=768, N=2048), FP8_Dynamic, at decode batches
-# of 1 and 32 tokens and a 512-token prefill.  Routing: each token picks 8
-# distinct experts uniformly (seeded); tokens are sorted by expert.
-MOE_LAYERS = [("gate_up", 2048, 1536), ("down", 768, 2048)]
-MOE_EXPERTS, MOE_TOPK = 128, 8
 MOE_BATCHES = [1, 32, 512]
 
 
@@ -354,8 +347,8 @@ def moe_points(reps: int = 8, target_bytes: int = 1 << 30):
     import synth
     dev = torch.device("cuda:0")
     out = []
-    for name, K, N in MOE_LAYERS:
-        E = MOE_EXPERTS
+    for name, K, N in synth.MOE_LAYERS:
+        E = synth.MOE_EXPERTS
         w = torch.from_numpy(np.ascontiguousarray(
             synth.rng(81, K, N).integers(0, 0x7E, (E, N, K), dtype=np.uint8) |
             (synth.rng(82, K, N).integers(0, 2, (E, N, K), dtype=np.uint8) << 7))).to(dev)
@@ -364,9 +357,7 @@ def moe_points(reps: int = 8, target_bytes: int = 1 << 30):
         copies = max(2, -(-target_bytes // (E * N * K)))
         ws = [w] + [w.clone() for _ in range(copies - 1)]
         for B in MOE_BATCHES:
-            g = synth.rng(83, B, K)
-            picks = np.stack([g.choice(E, MOE_TOPK, replace=False) for _ in range(B)])
-            counts = np.bincount(picks.ravel(), minlength=E)
+            counts = synth.moe_counts(B, K)
             rows = int(counts.sum())
             off = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
             a = torch.from_numpy(synth.rng(84, B, K).integers(0, 0x7E, (rows, K), dtype=np.uint8)).to(dev)

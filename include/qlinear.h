@@ -208,8 +208,10 @@ qlin_status qlin_grouped_scaled_mm(qlin_dtype dt, int64_t groups, const int32_t 
                                    int64_t b_group_stride, const float *b_scale,
                                    int64_t b_scale_group_stride, void *Y, int64_t ldy, void *stream,
                                    const qlin_config *cfg);
-/* The config a grouped call uses when given none: split_k = 1 and a kernel
- * chosen by the bound on rows per group (measured on 128-expert layers). */
+/* The config a grouped call uses when given none (split_k = 1): the table's
+ * grouped entry for (format, N, K) with the smallest rows-per-group bound
+ * >= max_rows (else the largest bound), tuned on 128-expert layers; for
+ * shapes without grouped entries, a kernel chosen by max_rows. */
 qlin_status qlin_select_grouped_config(qlin_scaling sc, qlin_dtype dt, int64_t max_rows,
                                        int64_t N, int64_t K, qlin_config *out);
 qlin_status qlin_grouped_block_scaled_mm(int64_t groups, const int32_t *group_offsets,
@@ -316,8 +318,10 @@ qlin_status qlin_kernel_instance(int32_t i, qlin_config *out, int32_t *fmt_mask)
  * the compiled-in table).  Format: one entry per line,
  *   <fmt> <N> <K> <M> <kernel> <variant> <tile_m> <tile_n> <tile_k>
  *   <waves_n> <waves_k> <stages> <split_k> <reduce>
- * with <fmt> one of fp8, int8, block_fp8; '#' starts a comment.  On error
- * the previous table is kept. */
+ * with <fmt> one of fp8, int8, block_fp8; '#' starts a comment.  A line
+ * starting with the word `grouped` (then the same fields, M being the bound
+ * on rows per expert and split_k 1) configures grouped calls.  On error the
+ * previous table is kept. */
 qlin_status qlin_load_config_table(const char *path);
 
 /* Number of entries in the active table. */

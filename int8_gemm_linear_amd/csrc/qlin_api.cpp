@@ -116,6 +116,7 @@ const Instance *find_instance(int fmt, int scal, const qlin_config &c)
 // ---------------------------------------------------------------------------
 struct Entry {
     int bit;
+    bool grouped;        // a grouped (mixture-of-experts) call; M = rows-per-expert bound
     int64_t N, K, M;
     qlin_config cfg;
 };
@@ -145,6 +146,9 @@ bool parse_table(const std::string &text, std::vector<Entry> &out)
         if (!(ls >> fmt))
             continue;  // blank or comment
         Entry e;
+        e.grouped = fmt == "grouped";
+        if (e.grouped && !(ls >> fmt))
+            return false;
         if (fmt == "fp8")
             e.bit = FB_FP8;
         else if (fmt == "int8")
@@ -162,6 +166,8 @@ bool parse_table(const std::string &text, std::vector<Entry> &out)
             return false;
         if (e.N <= 0 || e.K <= 0 || e.M <= 0)
             return false;
+        if (e.grouped && e.cfg.split_k != 1)
+            return false;   // grid.z of a grouped launch carries the expert
         t.push_back(e);
     }
     out.swap(t);
@@ -302,15 +308,15 @@ qlin_config default_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
 qlin_status check_config(int fmt, int scal, int64_t M, int64_t N, int64_t K,
                          const qlin_config &c, const Instance **inst);
 
-// Grouped (mixture-of-experts) calls: split_k = 1 (grid.z is the expert)
-// and a kernel chosen by the bound on rows per expert, from a sweep of every
-// instance over 128-expert layers (K, N) = (2048, 1536) and (768, 2048) at
-// 1-52 rows per expert: up to 3 rows the GEMV kernel when K >= 2048 (one or
-// two token rows per tile; at K = 768 its 2 KB row batches are mostly idle
-// lanes) and otherwise the LDS-ring stream kernel with 8-token tiles, the
-// register stream kernel with 16x64 tiles up to 16, a 64x128 tile up to 64
-// and a 128x128 tile beyond.  A choice the library lacks for the format
-// falls back to the table's config with split_k = 1.
+// Grouped (mixture-of-experts) calls: split_k = 1 (grid.z is the expert).
+// The config comes from the table's grouped entries, tuned per (format, N,
+// K, rows-per-expert bound) on 128-expert layers.  Shapes without entries
+// use a rule read off an earlier sweep of every instance over (K, N) =
+// (2048, 1536) and (768, 2048) at 1-52 rows per expert: up to 3 rows the
+// GEMV kernel when K >= 2048 and otherwise the LDS-ring stream kernel with
+// 8-token tiles, the register stream kernel with 16x64 tiles up to 16, a
+// 64x128 tile up to 64 and a 128x128 tile beyond; a choice the library
+// lacks for the format falls back to the table's config with split_k = 1.
 qlin_config grouped_config(int fmt, int scal, int64_t M, int64_t N, int64_t K);
 
 qlin_config select_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
@@ -318,7 +324,7 @@ qlin_config select_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
     const int bit = fmt_bit(fmt, scal);
     const Entry *best = nullptr, *largest = nullptr;
     for (const Entry &e : table()) {
-        if (e.bit != bit || e.N != N || e.K != K)
+        if (e.grouped || e.bit != bit || e.N != N || e.K != K)
             continue;
         if (e.M >= M && (!best || e.M < best->M))
             best = &e;
@@ -339,6 +345,22 @@ qlin_config select_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
 
 qlin_config grouped_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
 {
+    // Tuned entries first: the one for (fmt, N, K) with the smallest
+    // rows-per-expert bound >= M, else the largest bound.
+    const int bit = fmt_bit(fmt, scal);
+    const Entry *best = nullptr, *largest = nullptr;
+    for (const Entry &e : table()) {
+        if (!e.grouped || e.bit != bit || e.N != N || e.K != K)
+            continue;
+        if (e.M >= M && (!best || e.M < best->M))
+            best = &e;
+        if (!largest || e.M > largest->M)
+            largest = &e;
+    }
+    if (!best)
+        best = largest;
+    if (best && check_config(fmt, scal, M, N, K, best->cfg, nullptr) == QLIN_OK)
+        return best->cfg;
     auto make = [](int kernel, int tm, int tn, int tk, int wn, int wk, int st) {
         qlin_config c;
         std::memset(&c, 0, sizeof c);

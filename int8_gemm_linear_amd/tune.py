@@ -122,6 +122,54 @@ class Point:
         return float(np.median(ts))
 
 
+class GroupedPoint:
+    """Device inputs of one grouped (mixture-of-experts) layer call: E experts'
+    weights [E, N, K] (random finite codes, enough copies to be cold), the
+    token rows of a batch routed top-k by the seeded uniform routing and
+    sorted by expert, and the device offset table."""
+
+    def __init__(self, fmt, N, K, batch, cold_bytes=COLD_BYTES):
+        sys.path.insert(0, ROOT)
+        import synth
+        self.fmt, self.N, self.K, self.batch = fmt, N, K, batch
+        E = synth.MOE_EXPERTS
+        dev = torch.device("cuda")
+        counts = synth.moe_counts(batch, K)
+        self.rows = int(counts.sum())
+        self.M = int(counts.max())                       # the rows-per-expert bound
+        self.off = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
+        dt = torch.int8 if fmt == "int8" else torch.float8_e4m3fn
+        codes = synth.e4m3_codes((E, N, K), (91, K, N))
+        if fmt == "int8":
+            codes = (codes.view(np.int8) // 2).view(np.uint8)
+        b = torch.from_numpy(codes).to(dev).view(dt)
+        a = synth.e4m3_codes((self.rows, K), (92, batch, K))
+        self.a = torch.from_numpy((a.view(np.int8) // 2).view(np.uint8) if fmt == "int8" else a).to(dev).view(dt)
+        if fmt == "block_fp8":
+            self.sa = torch.full((self.rows, K // 128), 1e-2, device=dev)
+            self.sb = torch.full((E, N // 128, K // 128), 1e-3, device=dev)
+        else:
+            self.sa = torch.full((self.rows,), 1e-2, device=dev)
+            self.sb = torch.full((E, N), 1e-3, device=dev)
+        ncopy = int(min(16, max(2, -(-cold_bytes // (E * N * K)))))
+        self.b = [b] + [b.clone() for _ in range(ncopy - 1)]
+        self.y = torch.empty((self.rows, N), dtype=torch.bfloat16, device=dev)
+
+    def call(self, cfg, i=0, out=None):
+        f = q.grouped_block_scaled_mm if self.fmt == "block_fp8" else q.grouped_scaled_mm
+        return f(self.a, self.sa, self.b[i % len(self.b)], self.sb, self.off, self.M,
+                 out=self.y if out is None else out, config=cfg)
+
+    time = Point.time
+
+
+def grouped_candidates(fmt, M, N, K):
+    """Configs a grouped call can run: split_k = 1 (grid.z is the expert),
+    stream-kernel tiles of at most 4 token tiles, no spread placement."""
+    return [c for c in candidates(fmt, M, N, K, max_split=1)
+            if not (c.kernel == q.KERNEL_STREAM_LDS and c.waves_n == 2)]
+
+
 def agree(fmt, y, ref) -> bool:
     """Sanity check of a candidate against the reference candidate (parity
     itself is established by the tests against the oracle).  INT8: bit for
@@ -175,8 +223,42 @@ def tune_point(fmt, M, N, K, log=None, done=None, max_cands=None, verbose=False,
     return results
 
 
-def table_line(fmt, M, N, K, c) -> str:
-    return (f"{fmt} {N} {K} {M} {c.kernel} {c.variant} {c.tile_m} {c.tile_n} {c.tile_k} "
+def tune_grouped(fmt, N, K, batch, log=None, done=None, verbose=False):
+    """Times every grouped candidate of one layer call; returns (results, max_rows)."""
+    pt = GroupedPoint(fmt, N, K, batch)
+    M = pt.M
+    cands = grouped_candidates(fmt, M, N, K)
+    cur = q.select_grouped_config(fmt, M, N, K)
+    if cur not in cands:
+        cands = [cur] + cands
+    ref = pt.call(cur, out=torch.empty_like(pt.y)).clone()
+    torch.cuda.synchronize()
+    results = []
+    for c in cands:
+        key = json.dumps(["grouped", fmt, batch, N, K, list(c.__dict__.values())])
+        if done is not None and key in done:
+            results.append((done[key]["us"], c, done[key]["ok"]))
+            continue
+        y = pt.call(c, out=torch.full_like(pt.y, float("nan")))
+        torch.cuda.synchronize()
+        ok = agree(fmt, y, ref)
+        us = pt.time(c) if ok else float("inf")
+        results.append((us, c, ok))
+        if log is not None:
+            log.write(json.dumps({"key": key, "grouped": True, "fmt": fmt, "batch": batch, "M": M,
+                                  "N": N, "K": K, "cfg": c.__dict__, "us": us, "ok": ok}) + "\n")
+            log.flush()
+        if verbose:
+            print(f"  {us:9.2f} us ok={ok} {c}", flush=True)
+    results.sort(key=lambda r: r[0])
+    del pt
+    torch.cuda.empty_cache()
+    return results, M
+
+
+def table_line(fmt, M, N, K, c, grouped=False) -> str:
+    return (("grouped " if grouped else "") +
+            f"{fmt} {N} {K} {M} {c.kernel} {c.variant} {c.tile_m} {c.tile_n} {c.tile_k} "
             f"{c.waves_n} {c.waves_k} {c.stages} {c.split_k} {c.reduce}")
 
 
@@ -199,6 +281,10 @@ def main():
                     "(0 stream, 1 tile, 2 LDS-ring stream, 3 GEMV); the current pick is always kept")
     ap.add_argument("--max-split", type=int, default=256)
     ap.add_argument("--max-token-tiles", type=int, default=4)
+    ap.add_argument("--moe", default=None,
+                    help="comma list of formats: sweep the grouped call on the mixture-of-experts "
+                         "layers at the --moe-batches token counts")
+    ap.add_argument("--moe-batches", default="1,4,16,32,64,128,512,2048")
     ap.add_argument("--min-gain", type=float, default=0.02,
                     help="keep the current pick unless the best candidate is faster by this fraction "
                          "(timings of one run differ by about that much between candidates of equal speed)")
@@ -225,7 +311,23 @@ def main():
                 pass
     log = open(args.jsonl, "a") if args.jsonl else None
     best = {}
+    gbest = {}
     t0 = time.time()
+    for fmt in (args.moe.split(",") if args.moe else []):
+        for _, K, N in synth.MOE_LAYERS:
+            for batch in (int(b) for b in args.moe_batches.split(",")):
+                res, M = tune_grouped(fmt, N, K, batch, log=log, done=done, verbose=args.verbose)
+                us, c, _ = res[0]
+                cur = q.select_grouped_config(fmt, M, N, K)
+                cus = next((r[0] for r in res if r[1] == cur), float("nan"))
+                if cus == cus and us > cus * (1.0 - args.min_gain):
+                    us, c = cus, cur
+                if (fmt, M, N, K) in gbest and gbest[(fmt, M, N, K)][0] <= us:
+                    continue
+                gbest[(fmt, M, N, K)] = (us, c)
+                print(f"[tune] grouped {fmt:9s} batch={batch:5d} max_rows={M:4d} N={N:6d} K={K:6d}: "
+                      f"best {us:8.2f} us current {cus:8.2f} us | {len(res)} cands | "
+                      f"{table_line(fmt, M, N, K, c, grouped=True)} [{time.time() - t0:.0f}s]", flush=True)
     for (fmt, M, N, K) in points:
         res = tune_point(fmt, M, N, K, log=log, done=done, max_cands=args.max_cands,
                          verbose=args.verbose, **sel)
@@ -244,10 +346,14 @@ def main():
         if os.path.exists(args.table):
             for ln in open(args.table):
                 s = ln.split("#")[0].split()
+                g = bool(s) and s[0] == "grouped"
+                s = s[1:] if g else s
                 if len(s) == 14:
-                    lines[(s[0], int(s[3]), int(s[1]), int(s[2]))] = ln.strip()
+                    lines[(g, s[0], int(s[3]), int(s[1]), int(s[2]))] = ln.strip()
         for (fmt, M, N, K), c in best.items():
-            lines[(fmt, M, N, K)] = table_line(fmt, M, N, K, c)
+            lines[(False, fmt, M, N, K)] = table_line(fmt, M, N, K, c)
+        for (fmt, M, N, K), (_, c) in gbest.items():
+            lines[(True, fmt, M, N, K)] = table_line(fmt, M, N, K, c, grouped=True)
         hdr = [ln.rstrip("\n") for ln in open(args.table) if ln.startswith("#")] \
             if os.path.exists(args.table) else []
         with open(args.table, "w") as f:

@@ -219,5 +219,27 @@ def workload(name: str):
     raise KeyError(name)
 
 
+# Mixture-of-experts layers of a 30B-class model with 3B active parameters
+# (hidden 2048, 128 experts, 8 per token, expert width 768): gate_up
+# (K=2048, N=1536) and down (K=768, N=2048), as (name, K, N).  Routing: each
+# token picks 8 distinct experts uniformly (seeded); tokens sorted by expert.
+MOE_LAYERS = (("gate_up", 2048, 1536), ("down", 768, 2048))
+MOE_EXPERTS, MOE_TOPK = 128, 8
+
+
+def moe_counts(batch: int, K: int, experts: int = MOE_EXPERTS, topk: int = MOE_TOPK) -> np.ndarray:
+    """Rows per expert for a batch of tokens under seeded uniform top-k routing."""
+    g = rng(83, batch, K)
+    picks = np.stack([g.choice(experts, topk, replace=False) for _ in range(batch)])
+    return np.bincount(picks.ravel(), minlength=experts)
+
+
+def e4m3_codes(shape, key) -> np.ndarray:
+    """Random finite e4m3 codes of both signs (timing inputs: no NaN codes)."""
+    g = rng(*key)
+    return (g.integers(0, 0x7E, shape, dtype=np.uint8) |
+            (g.integers(0, 2, shape, dtype=np.uint8) << 7)).astype(np.uint8)
+
+
 WORKLOADS = ("fp8_small", "int8_1p7b_decode", "fp8_8b", "block_fp8_8b", "all_32b", "all_32b_decode",
              "prefill")

@@ -213,10 +213,16 @@ def test_compiled_in_table_entries_are_valid():
         f = ln.split("#")[0].split()
         if not f:
             continue
+        grouped = f[0] == "grouped"
+        f = f[1:] if grouped else f
         fmt, N, K, M = f[0], int(f[1]), int(f[2]), int(f[3])
         c = q.Config(*[int(x) for x in f[4:14]])
         assert q.check_config(fmt, M, N, K, c) == 0, ln
-        assert q.select_config(fmt, M, N, K) == c, ln
+        if grouped:
+            assert c.split_k == 1, ln
+            assert q.select_grouped_config(fmt, M, N, K) == c, ln
+        else:
+            assert q.select_config(fmt, M, N, K) == c, ln
         n += 1
     assert n == q.config_table_size()
 
@@ -339,10 +345,13 @@ def test_grouped_default_config_is_valid_and_unsplit():
                 c = q.select_grouped_config(fmt, mr, N, K)
                 assert c.split_k == 1, (fmt, mr, c)
                 assert q.check_config(fmt, mr, N, K, c) == 0, (fmt, mr, N, K, c)
-                # the rule: GEMV for at most 3 rows per expert at K >= 2048
+                # shapes without grouped table entries follow the built-in
+                # rule: GEMV for at most 3 rows per expert at K >= 2048
                 # (token/channel formats), the LDS-ring kernel below that K
-                if mr <= 3 and fmt != "block_fp8":
-                    assert c.kernel == (q.KERNEL_GEMV if K >= 2048 else q.KERNEL_STREAM_LDS), (fmt, mr, K, c)
+                if (N, K) == (256, 1024) and mr <= 3 and fmt != "block_fp8":
+                    assert c.kernel == q.KERNEL_STREAM_LDS, (fmt, mr, K, c)
+    # (K, N) = (2048, 4096) has no grouped entries either
+    assert q.select_grouped_config("fp8", 2, 4096, 2048).kernel == q.KERNEL_GEMV
 
 
 def test_noalloc_validation_and_workspace_limit():
@@ -372,3 +381,32 @@ def oversize_shape():
         if q.workspace_size(fmt, M, N, K) > 32 << 20:
             return fmt, M, N, K
     raise AssertionError("no candidate shape needs more than 32 MiB of split-K workspace")
+
+
+def test_grouped_table_entries(tmp_path):
+    # A `grouped` line configures grouped calls only, keyed by the bound on
+    # rows per expert (smallest tuned bound >= max_rows, else the largest).
+    N, K = 1536, 2048
+    path = tmp_path / "t.cfg"
+    path.write_text(
+        "grouped fp8 1536 2048 4 2 1 8 16 512 1 4 4 1 1\n"
+        "grouped fp8 1536 2048 64 1 1 64 128 128 1 4 4 1 1\n"
+        "fp8 1536 2048 4 0 1 16 16 512 1 4 2 1 1\n")
+    try:
+        q.load_config_table(str(path))
+        c = q.select_grouped_config("fp8", 3, N, K)
+        assert (c.kernel, c.tile_m, c.tile_n) == (q.KERNEL_STREAM_LDS, 8, 16)
+        c = q.select_grouped_config("fp8", 5, N, K)
+        assert (c.kernel, c.tile_m, c.tile_n) == (q.KERNEL_TILE, 64, 128)
+        c = q.select_grouped_config("fp8", 500, N, K)          # past the largest bound
+        assert (c.kernel, c.tile_m) == (q.KERNEL_TILE, 64)
+        c = q.select_config("fp8", 4, N, K)                    # ordinary calls ignore grouped lines
+        assert (c.kernel, c.tile_k) == (q.KERNEL_STREAM, 512)
+        # a grouped line with split_k != 1 is malformed: the table is kept
+        bad = tmp_path / "bad.cfg"
+        bad.write_text("grouped fp8 1536 2048 4 2 1 8 16 512 1 4 4 2 1\n")
+        with pytest.raises(q.QlinError):
+            q.load_config_table(str(bad))
+        assert q.config_table_size() == 3
+    finally:
+        q.load_config_table(None)

@@ -34,12 +34,15 @@ def say(*a):
     sys.stdout.flush()
 
 
-def table_entries():
+def table_entries(grouped=False):
+    """(fmt, M, N, K, Config) of every ordinary (or every grouped) table line."""
     out = []
     for line in open(TABLE):
         line = line.split("#", 1)[0].split()
-        if not line:
+        if not line or (line[0] == "grouped") != grouped:
             continue
+        if grouped:
+            line = line[1:]
         fmt = line[0]
         N, K, M = (int(v) for v in line[1:4])
         cfg = q.Config(*(int(v) for v in line[4:14]))
@@ -82,7 +85,7 @@ def test_table_has_every_workload_point():
     pts = {p for w in ("fp8_small", "int8_1p7b_decode", "fp8_8b", "block_fp8_8b", "all_32b")
            for p in synth.workload(w)}
     assert {(f, M, N, K) for (f, M, N, K, _) in ENTRIES} == pts
-    assert len(ENTRIES) == q.config_table_size()
+    assert len(ENTRIES) + len(table_entries(grouped=True)) == q.config_table_size()
 
 
 @pytest.mark.parametrize("fmt,M,N,K,cfg", ENTRIES,

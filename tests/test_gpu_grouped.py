@@ -181,3 +181,69 @@ def test_all_groups_empty_and_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         check("fp8", parity.y_bits(out), qa, sa, qb, sb, o, 8, f"replay {routing}")
+
+
+# ---------------------------------------------------------------------------
+# Every grouped entry of the tuned table at its full size: a 128-expert top-8
+# layer of the 30B-class mixture-of-experts model, routed by the seeded
+# uniform routing at the token count the entry was tuned on, with real
+# quantized weights; the library's own selection must be the entry's config.
+# Checked at 1500 sampled outputs (plus every expert's first and last row).
+# ---------------------------------------------------------------------------
+import functools
+import os
+
+from tests.test_gpu_full_size import table_entries
+
+GROUPED_ENTRIES = table_entries(grouped=True)
+TUNED_BATCHES = (1, 4, 16, 32, 64, 128, 512, 2048)
+
+
+@functools.lru_cache(maxsize=1)
+def moe_weights(fmt, N, K):
+    E = synth.MOE_EXPERTS
+    qb, sb = [], []
+    for e in range(E):
+        w = synth.weights(N, K, (72, e, N, K))
+        b, s = synth.quant_blocks(w) if fmt == "block_fp8" else synth.quant_rows(w, fmt)
+        qb.append(b)
+        sb.append(s)
+    return np.stack(qb), np.stack(sb).astype(np.float32)
+
+
+def batch_for(M, K):
+    for b in TUNED_BATCHES:
+        if int(synth.moe_counts(b, K).max()) == M:
+            return b
+    raise AssertionError(f"no tuned batch routes at most {M} rows to an expert (K={K})")
+
+
+@pytest.mark.parametrize("fmt,M,N,K,cfg", GROUPED_ENTRIES,
+                         ids=[f"{f}-rows{M}-N{N}-K{K}" for (f, M, N, K, _) in GROUPED_ENTRIES])
+def test_grouped_table_entry_full_size(fmt, M, N, K, cfg):
+    sel = q.select_grouped_config(fmt, M, N, K)
+    assert sel == cfg, f"the library selects {sel}, the table says {cfg}"
+    batch = batch_for(M, K)
+    counts = synth.moe_counts(batch, K)
+    rows = int(counts.sum())
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = synth.activations(rows, K, (73, batch, K), outliers=fmt != "int8", outlier_key=(73, 3, K))
+    qa, sa = synth.quant_groups(x) if fmt == "block_fp8" else synth.quant_rows(x, fmt)
+    qb, sb = moe_weights(fmt, N, K)
+    say("grouped full", fmt, "batch", batch, "max_rows", M, (N, K), cfg)
+    y = run(fmt, to_dev(fmt, qa, sa, qb, sb, off), M)
+    # sampled positions: every active expert's first and last row, then random rows
+    g = np.random.default_rng(5)
+    act = [e for e in range(len(counts)) if counts[e] > 0]
+    ms = [int(off[e]) for e in act] + [int(off[e + 1]) - 1 for e in act]
+    ms += list(g.integers(0, rows, 1500))
+    ns = list(g.integers(0, N, len(ms)))
+    ms, ns = np.asarray(ms), np.asarray(ns)
+    expert = np.searchsorted(off, ms, side="right") - 1
+    block = fmt == "block_fp8"
+    for e in np.unique(expert):
+        sel_e = expert == e
+        lo = int(off[e])
+        r = oracle.scaled_mm_points(parity.FMT_CODE[fmt], qa[lo:int(off[e + 1])], sa[lo:int(off[e + 1])],
+                                    qb[e], sb[e], ms[sel_e] - lo, ns[sel_e], block=block)
+        parity.check_y(fmt, y[ms[sel_e], ns[sel_e]], r.y, r.ydbl, r.bound, f"{fmt} expert {e}")
