@@ -253,7 +253,9 @@ __device__ inline void quantize_row(const u32x4 (&y)[kReg], int P, uint8_t *qrow
     }
 }
 
-template <int OP, int QM, int W, bool RES>
+// SKIP (SiLU-and-mul only): register slots past the row's end are not
+// evaluated (they hold zeros, which would take the exact double path).
+template <int OP, int QM, int W, bool RES, bool SKIP = false>
 __global__ void __launch_bounds__(64 * W)
 k_rows(RowArgs a)
 {
@@ -285,7 +287,8 @@ k_rows(RowArgs a)
         }
 #pragma unroll
         for (int i = 0; i < kReg; ++i)
-            y[i] = silu8(y[i], gu[i]);
+            if (!SKIP || t + i * NT < P)
+                y[i] = silu8(y[i], gu[i]);
         quantize_row<QM, W>(y, P, qrow, srow, [&](int p) { return silu8(x[p], u[p]); });
     } else {
         u32x4 *r = RES ? reinterpret_cast<u32x4 *>(a.R + (int64_t)row * a.ldr) : nullptr;
@@ -345,22 +348,25 @@ inline int waves_for(int64_t M, int64_t K)
     return w;
 }
 
-// Waves per SiLU-and-mul row: only the fewest that hold the row's pieces in
-// registers, at most 4.  Every lane runs all kReg register slots, and a
-// slot past the row's end (zeros) takes the exact double-precision path
-// (zero fails the fast path's range test), so spreading a short row over
-// more waves lengthens each lane's chain instead of shortening it
-// (measured, same codes and scales: M = 32, K = 4096 on one wave 11.9 us,
-// on four 21.5 us; M = 1 10.4 against 20.6 us).  At most 4: the kernels
+// Waves per SiLU-and-mul row.  With rows enough to fill the machine, the
+// fewest that hold the row's pieces in registers, at most 4 (the kernels
 // need ~125 registers, so an 8-wave workgroup would leave room for only one
-// per CU; longer rows recompute the pieces past the register window
-// (measured faster: 113 vs 134 us at 2048 x 25600).
-inline int silu_waves(int64_t K)
+// per CU; longer rows recompute the pieces past the register window:
+// measured faster, 113 vs 134 us at 2048 x 25600); every lane then runs all
+// kReg slots.  With few rows (fewer than 2048 waves in the grid: decode)
+// the row is spread over up to 8 waves to shorten each lane's serial chain,
+// and the slots past the row's end are skipped (`skip`): evaluated, their
+// zeros would take the exact double path, which made wider rows slower.
+inline int silu_waves(int64_t M, int64_t K, bool *skip)
 {
     const int64_t P = K >> 3;
     int w = 1;
     while (w < 4 && (int64_t)64 * w * kReg < P)
         w *= 2;
+    const int fewest = w;
+    while (w < kMaxW && M * w < 2048 && (int64_t)64 * w < P)
+        w *= 2;
+    *skip = w > fewest;
     return w;
 }
 
@@ -368,7 +374,18 @@ template <int OP, int QM, bool RES>
 hipError_t launch_rows(const RowArgs &a, int64_t M, hipStream_t s)
 {
     const dim3 grid((unsigned)M);
-    const int w = OP == OP_SILU ? silu_waves(a.K) : waves_for(M, a.K);
+    bool skip = false;
+    const int w = OP == OP_SILU ? silu_waves(M, a.K, &skip) : waves_for(M, a.K);
+    if constexpr (OP == OP_SILU) {
+        if (skip) {
+            switch (w) {
+            case 2: hipLaunchKernelGGL((k_rows<OP, QM, 2, RES, true>), grid, dim3(128), 0, s, a); break;
+            case 4: hipLaunchKernelGGL((k_rows<OP, QM, 4, RES, true>), grid, dim3(256), 0, s, a); break;
+            default: hipLaunchKernelGGL((k_rows<OP, QM, 8, RES, true>), grid, dim3(512), 0, s, a); break;
+            }
+            return hipGetLastError();
+        }
+    }
     switch (w) {
     case 1: hipLaunchKernelGGL((k_rows<OP, QM, 1, RES>), grid, dim3(64), 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_rows<OP, QM, 2, RES>), grid, dim3(128), 0, s, a); break;
