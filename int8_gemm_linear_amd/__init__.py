@@ -184,6 +184,7 @@ def lib():
 # ---------------------------------------------------------------------------
 _WS: dict = {}
 _WS_KEPT: list = []
+COUNTER_BYTES = 128 * 1024      # the workspace's leading counter region (include/qlinear.h)
 
 
 def _capture_id(stream) -> int:
@@ -207,7 +208,10 @@ def workspace_for(nbytes: int, device: torch.device, stream=None) -> torch.Tenso
     if buf is None or buf.numel() < nbytes:
         size = max(nbytes, 1 << 20, 2 * buf.numel() if buf is not None else 0)
         with torch.cuda.stream(stream):
-            new = torch.zeros(size, dtype=torch.uint8, device=torch.device("cuda", dev))
+            # only the counter region must start at zero (a fill kernel; the
+            # split partials are always written before they are read)
+            new = torch.empty(size, dtype=torch.uint8, device=torch.device("cuda", dev))
+            new[:COUNTER_BYTES].zero_()
         if buf is not None:
             _WS_KEPT.append(buf)
         _WS[key] = buf = new
