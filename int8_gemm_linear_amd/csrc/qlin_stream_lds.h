@@ -65,6 +65,22 @@ __device__ inline void wait_vm()
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// s_waitcnt vmcnt(L * min(n, NMAX)) for a run-time n >= 0: wait until at
+// most n chunks' copies (L per chunk) are still in flight.
+template <int L, int NMAX>
+__device__ inline void wait_chunks(int n)
+{
+    if constexpr (NMAX > 0) {
+        if (n >= NMAX) {
+            wait_vm<L * NMAX>();
+            return;
+        }
+        wait_chunks<L, NMAX - 1>(n);
+    } else {
+        wait_vm<0>();
+    }
+}
+
 template <int FMT, int SCAL, bool SWAP, int TMS, int TRW, int NW, int S, int CHK>
 __global__ void __launch_bounds__(64 * NW)
 k_stream_lds(KArgs p_)
@@ -93,7 +109,7 @@ k_stream_lds(KArgs p_)
     constexpr int L = L0 + LS;                       // copies per wave per chunk
     static_assert(CHK == 512 || CHK == 1024, "chunk");
     static_assert(TMS >= 1 && TMS <= 32, "tokens per tile");
-    static_assert(S >= 1 && S <= 4 && L * (S - 1) <= 63, "ring");
+    static_assert(S >= 1 && S <= 8 && L * (S - 1) <= 63, "ring");
     static_assert(!BLK || FMT == FMT_E4M3, "block scaling is e4m3 only");
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[S * STAGE];
@@ -269,15 +285,7 @@ k_stream_lds(KArgs p_)
         sb_at[rb] = TMS * GPC + (((n0 + rb * 16 + (SWAP ? 4 * g : r16)) >> 7) - (n0 >> 7)) * GPC;
 
     for (int c = 0; c < nch; ++c) {
-        const int after = min(S - 1, nch - 1 - c);   // chunks issued after c
-        if (after >= 3)
-            wait_vm<L * 3>();
-        else if (after == 2)
-            wait_vm<L * 2>();
-        else if (after == 1)
-            wait_vm<L>();
-        else
-            wait_vm<0>();
+        wait_chunks<L, S - 1>(nch - 1 - c);           // chunks issued after c stay in flight
         __syncthreads();
         const uint8_t *st = lds + (c % S) * STAGE;
         const int steps = min(CHK, kend - (kbeg + c * CHK)) >> 7;

@@ -317,3 +317,30 @@ def test_spread_row_placement(fmt):
                     yb = parity.y_bits(y)
                     first = yb if first is None else first
                     assert np.array_equal(yb, first), f"int8 disagreement at {cc}"
+
+
+@pytest.mark.parametrize("fmt", ["int8", "fp8", "block_fp8"])
+def test_deep_rings_long_k(fmt):
+    # Every LDS-ring instance with three or more stages on a K long enough to
+    # cycle its ring several times (K = 12288: 12-24 chunks), both placements,
+    # with and without split-K.
+    M, N, K = 20, (384 if fmt == "block_fp8" else 300), 12288
+    case = small_case(fmt, M, N, K, root=25)
+    ref = small_ref(fmt, M, N, K, root=25)
+    dev = parity.to_device(case)
+    first = None
+    for c in q.instances_for(fmt):
+        if c.kernel != q.KERNEL_STREAM_LDS or c.stages < 3 or -(-M // c.tile_m) > 4:
+            continue
+        for split, red in ((1, 1), (2, q.REDUCE_TWO_PASS)):
+            cc = c.replace(split_k=split, reduce=red)
+            if q.check_config(fmt, M, N, K, cc) != 0:
+                continue
+            say("deep ring", fmt, cc)
+            y = call(case, dev, cc)
+            torch.cuda.synchronize()
+            parity.check_case(case, y, ref, what=f"{fmt} {cc}")
+            if fmt == "int8":
+                yb = parity.y_bits(y)
+                first = yb if first is None else first
+                assert np.array_equal(yb, first), f"int8 disagreement at {cc}"
