@@ -20,6 +20,7 @@
 #include <mutex>
 #include <sstream>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "qlin_internal.h"
@@ -125,7 +126,29 @@ struct Entry {
 // takes a lock; a replacement installs a new table and keeps every earlier
 // one alive until the process ends, so a lookup that raced a replacement
 // still reads valid memory (tables are a few KB and replaced rarely).
-typedef std::vector<Entry> Table;
+// Entries with an index from (grouped, format, N, K) to that shape's entries,
+// so a lookup visits only the handful of tuned token counts of its shape.
+struct Table {
+    std::vector<Entry> entries;
+    std::unordered_map<uint64_t, std::vector<const Entry *>> by_shape;
+    size_t size() const { return entries.size(); }
+};
+
+uint64_t shape_key(bool grouped, int bit, int64_t N, int64_t K)
+{
+    return ((((uint64_t)grouped << 3 | (uint64_t)bit) << 25 | (uint64_t)N) << 21) | (uint64_t)K;
+}
+
+const std::vector<const Entry *> &entries_of(const Table &t, bool grouped, int bit, int64_t N,
+                                             int64_t K)
+{
+    static const std::vector<const Entry *> none;
+    if (N <= 0 || N > kMaxMN || K <= 0 || K > kMaxK)
+        return none;
+    const auto it = t.by_shape.find(shape_key(grouped, bit, N, K));
+    return it == t.by_shape.end() ? none : it->second;
+}
+
 std::atomic<const Table *> g_table{nullptr};
 std::once_flag g_table_once;
 std::mutex g_table_mutex;                       // serialises replacements
@@ -174,10 +197,15 @@ bool parse_table(const std::string &text, std::vector<Entry> &out)
     return true;
 }
 
-void install_table(Table t)
+void install_table(std::vector<Entry> entries)
 {
+    std::unique_ptr<Table> t(new Table);
+    t->entries = std::move(entries);
+    for (const Entry &e : t->entries)
+        if (e.N <= kMaxMN && e.K <= kMaxK)
+            t->by_shape[shape_key(e.grouped, e.bit, e.N, e.K)].push_back(&e);
     std::lock_guard<std::mutex> lk(g_table_mutex);
-    g_tables.push_back(std::unique_ptr<Table>(new Table(std::move(t))));
+    g_tables.push_back(std::move(t));
     g_table.store(g_tables.back().get(), std::memory_order_release);
 }
 
@@ -188,7 +216,7 @@ const Table &table()
     std::call_once(g_table_once, [] {
         const char *e = std::getenv("QLIN_LOG");
         g_log.store((e && *e && *e != '0') ? 1 : 0, std::memory_order_relaxed);
-        Table t;
+        std::vector<Entry> t;
         bool ok = false;
         const char *path = std::getenv("QLIN_CONFIG");
         if (path && *path) {
@@ -323,13 +351,11 @@ qlin_config select_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
 {
     const int bit = fmt_bit(fmt, scal);
     const Entry *best = nullptr, *largest = nullptr;
-    for (const Entry &e : table()) {
-        if (e.grouped || e.bit != bit || e.N != N || e.K != K)
-            continue;
-        if (e.M >= M && (!best || e.M < best->M))
-            best = &e;
-        if (!largest || e.M > largest->M)
-            largest = &e;
+    for (const Entry *e : entries_of(table(), false, bit, N, K)) {
+        if (e->M >= M && (!best || e->M < best->M))
+            best = e;
+        if (!largest || e->M > largest->M)
+            largest = e;
     }
     // Beyond the tuned M range the largest entry is used, unless the call is
     // a prefill far past tables tuned only for decode (M <= 64), where a
@@ -349,13 +375,11 @@ qlin_config grouped_config(int fmt, int scal, int64_t M, int64_t N, int64_t K)
     // rows-per-expert bound >= M, else the largest bound.
     const int bit = fmt_bit(fmt, scal);
     const Entry *best = nullptr, *largest = nullptr;
-    for (const Entry &e : table()) {
-        if (!e.grouped || e.bit != bit || e.N != N || e.K != K)
-            continue;
-        if (e.M >= M && (!best || e.M < best->M))
-            best = &e;
-        if (!largest || e.M > largest->M)
-            largest = &e;
+    for (const Entry *e : entries_of(table(), true, bit, N, K)) {
+        if (e->M >= M && (!best || e->M < best->M))
+            best = e;
+        if (!largest || e->M > largest->M)
+            largest = e;
     }
     if (!best)
         best = largest;
