@@ -112,6 +112,19 @@ __device__ inline void lds_dma16(const void *g, const void *lds)
                  : "memory", "m0");
 }
 
+// As lds_dma16, with the non-temporal cache policy: for weight bytes that
+// are read once per launch (streamed past L2 rather than kept there).  A
+// plain read of a 262 MB weight matrix through LDS runs about 7% faster
+// this way on MI355X.
+__device__ inline void lds_dma16_nt(const void *g, const void *lds)
+{
+    const unsigned off = (unsigned)(size_t)lds;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(off))
+                 : "memory", "m0");
+}
+
 // Copy 4 bytes per lane HBM/L2 -> LDS (global_load_lds_dword): lane i's
 // bytes land at lds + 4*i.  Same contract as lds_dma16 (inline assembly, no
 // register output, the caller counts its own copies in vmcnt).

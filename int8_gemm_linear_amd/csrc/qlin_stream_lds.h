@@ -8,7 +8,7 @@
 // The LDS round trip costs nothing that matters here: LDS bandwidth is far
 // above a CU's share of HBM bandwidth.
 //
-// Workgroup: NW waves own TR = 8, 16, 32, 48, 64, 96 or 128 weight rows (the matrix core sees
+// Workgroup: NW waves own TR = 8, 16, 32, 48, 64, 96, 112 or 128 weight rows (the matrix core sees
 // blocks of 16; with 8 rows, fragment rows 8..15 repeat rows 0..7 and their
 // outputs are dropped, which doubles the workgroup count for small N without
 // a split-K reduction) and TMS tokens (1..32; the
@@ -23,7 +23,9 @@
 // (for decode K this is usually the whole split: one round trip), and stage
 // c % S is refilled with chunk c + S after chunk c is consumed.  All global
 // loads inside the loop are these copies, so the wait for chunk c is an
-// exact s_waitcnt vmcnt(L * chunks issued after c).
+// exact s_waitcnt vmcnt(L * chunks issued after c).  Weight rows are copied
+// with the non-temporal policy (streamed once), token rows with the default
+// one (every workgroup re-reads them from L2).
 //
 // LDS swizzle: within a row, 16-byte slot s holds the chunk's 16-byte piece
 // s ^ (row & 15).  A matrix-core fragment read (16 lanes, 16 consecutive
@@ -91,7 +93,8 @@ k_stream_lds(KArgs p_)
     constexpr int TR = TRW;                          // weight rows of the workgroup
     constexpr int RB = TR >= 16 ? TR / 16 : 1;       // 16-row matrix-core blocks
     constexpr int RMASK = TR >= 16 ? 15 : TR - 1;    // fragment row within the stage
-    static_assert(TR == 8 || TR == 16 || TR == 32 || TR == 48 || TR == 64 || TR == 96 || TR == 128,
+    static_assert(TR == 8 || TR == 16 || TR == 32 || TR == 48 || TR == 64 || TR == 96 || TR == 112 ||
+                      TR == 128,
                   "weight rows");
     constexpr int RPI = 1024 / CHK;                  // rows per load instruction
     constexpr int ROWS0 = TR + TMS;
@@ -153,6 +156,11 @@ k_stream_lds(KArgs p_)
     // -- keeping the per-wave load count exact for the vmcnt waits -- but all
     // lanes read the same 16 bytes: one cache line instead of a 1 KB segment.
     const uint8_t *src[L0];
+    // Bit i: copy i of this wave brings weight rows (all of its rows are
+    // weight rows or none are: TR is a multiple of 8).  Derived from the
+    // wave index through readfirstlane, so the choice of copy instruction
+    // below is a scalar branch and every wave issues exactly one copy per i.
+    unsigned wmask = 0;
 #pragma unroll
     for (int i = 0; i < L0; ++i) {
         const int ins = wave + i * NW;
@@ -164,7 +172,10 @@ k_stream_lds(KArgs p_)
         const uint8_t *base = isb ? p.B + (int64_t)(valid ? row : 0) * p.ldb
                                   : p.A + (int64_t)(valid ? row : 0) * p.lda;
         src[i] = valid ? base + 16 * (slot ^ (j & 15)) : base;
+        if (ins * RPI < TR)
+            wmask |= 1u << i;
     }
+    wmask = __builtin_amdgcn_readfirstlane(wmask);
 
     // Block scaling: per scale copy, the source of this lane's dword for the
     // split's first chunk (chunk c adds c * GPC), its group within the chunk,
@@ -204,8 +215,14 @@ k_stream_lds(KArgs p_)
 #pragma unroll
         for (int i = 0; i < L0; ++i) {
             const int ins = wave + i * NW;
-            if (slot * 16 < len)
-                lds_dma16(src[i] + k0, st + ins * 1024);
+            // weight rows: non-temporal (read once per launch); token rows
+            // keep the default policy (every workgroup re-reads them from L2)
+            if (slot * 16 < len) {
+                if ((wmask >> i) & 1u)
+                    lds_dma16_nt(src[i] + k0, st + ins * 1024);
+                else
+                    lds_dma16(src[i] + k0, st + ins * 1024);
+            }
         }
         if constexpr (BLK) {
             const int glen = len >> 7;                 // groups in this chunk
@@ -563,6 +580,7 @@ hipError_t launch_stream_lds(const KArgs &a, dim3 grid, hipStream_t s)
 #define QLIN_STREAM_LDS_WIDE(X, FMT, BIT, SW)      \
     X(FMT, BIT, SW, 16, 96, 8, 2, 512),            \
     X(FMT, BIT, SW, 32, 96, 8, 2, 512),            \
+    X(FMT, BIT, SW, 32, 112, 8, 2, 512),           \
     X(FMT, BIT, SW, 16, 128, 8, 2, 512)
 
 }  // namespace qlin

@@ -456,6 +456,17 @@ k_tile(KArgs p_)
         }
         src[i] = base + 16 * ((lane & 7) ^ lds_swz(r));
     }
+    // Bit i: copy i of this wave brings weight rows (a group is all token or
+    // all weight rows: BM is a multiple of 8) and the weights are read by
+    // this workgroup alone (one token tile: decode), so it streams them with
+    // the non-temporal policy; with several token tiles the workgroups of a
+    // weight tile share it through L2 and the copy keeps the default policy.
+    unsigned ntmask = 0;
+#pragma unroll
+    for (int i = 0; i < GPW; ++i)
+        if ((wave + i * NW) * 8 >= BM && p.M <= BM)
+            ntmask |= 1u << i;
+    ntmask = __builtin_amdgcn_readfirstlane(ntmask);
 
     static_assert(ROWS / 8 % NW == 0, "copies must split evenly over the waves");
     constexpr int L = GPW + LSC;                      // copies per wave per step
@@ -481,8 +492,12 @@ k_tile(KArgs p_)
 #pragma unroll
         for (int i = 0; i < GPW; ++i) {
             const int grp_i = wave + i * NW;
-            if (GROUPS % NW == 0 || grp_i < GROUPS)
-                lds_dma16(src[i] + (int64_t)st * 128, dst0 + grp_i * 1024);
+            if (GROUPS % NW == 0 || grp_i < GROUPS) {
+                if ((ntmask >> i) & 1u)
+                    lds_dma16_nt(src[i] + (int64_t)st * 128, dst0 + grp_i * 1024);
+                else
+                    lds_dma16(src[i] + (int64_t)st * 128, dst0 + grp_i * 1024);
+            }
         }
         if constexpr (BLK) {
 #pragma unroll
