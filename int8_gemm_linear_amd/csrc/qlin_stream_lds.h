@@ -113,6 +113,7 @@ k_stream_lds(KArgs p_)
     static_assert(CHK == 512 || CHK == 1024, "chunk");
     static_assert(TMS >= 1 && TMS <= 32, "tokens per tile");
     static_assert(S >= 1 && S <= 8 && L * (S - 1) <= 63, "ring");
+    static_assert(S * STAGE <= 160 * 1024, "LDS per workgroup");
     static_assert(!BLK || FMT == FMT_E4M3, "block scaling is e4m3 only");
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[S * STAGE];
@@ -508,7 +509,9 @@ k_stream_lds(KArgs p_)
     if (!la)
         return;
     const int tile = blockIdx.y * gridDim.x + blockIdx.x;
-    if (!arrive_last(p.counters + tile, p.split_k))
+    // the flag lives in the ring: wave 0's last read of it (the combine)
+    // precedes the barrier inside arrive_last
+    if (!arrive_last(p.counters + tile, p.split_k, reinterpret_cast<int *>(lds)))
         return;
     if (wave == 0) {
         A4 sum[RB][TB];
