@@ -135,8 +135,10 @@ __device__ inline bool tile_in_group(const KArgs &p)
 // either scaled, rounded and stored (no split), or written as split-K
 // partials; with the last-arriver reduction the last workgroup of the tile
 // sums the partials in split order and stores the result.
+// Always inlined: an out-of-line call (it has two callers per tile shape,
+// the kernel's two copy forms) saves the live accumulators to scratch.
 template <int FMT, int SCAL, bool SWAP, int BM, int BN, int WM, int WN>
-__device__ inline void tile_finish(const KArgs &p,
+__device__ inline __attribute__((always_inline)) void tile_finish(const KArgs &p,
                                    typename AccT<FMT>::v16 (&acc)[BM / WM / 32][BN / WN / 32],
                                    int m0, int n0, int wm, int wn, int lane, uint8_t *lds)
 {
@@ -390,7 +392,12 @@ __device__ inline void tile_finish(const KArgs &p,
     emit(acc);
 }
 
-template <int FMT, int SCAL, bool SWAP, int BM, int BN, int WM, int WN, int S>
+// NTB: the launch has one token tile (M <= BM: decode), so every weight
+// tile is read by one workgroup and its copies use the non-temporal policy;
+// with several token tiles the workgroups of a weight tile share it through
+// L2 and the copies keep the default policy.  A template parameter, so the
+// prefill form of the copy loop carries no extra branch.
+template <int FMT, int SCAL, bool SWAP, int BM, int BN, int WM, int WN, int S, bool NTB>
 __global__ void __launch_bounds__(64 * WM * WN)
 k_tile(KArgs p_)
 {
@@ -456,17 +463,18 @@ k_tile(KArgs p_)
         }
         src[i] = base + 16 * ((lane & 7) ^ lds_swz(r));
     }
-    // Bit i: copy i of this wave brings weight rows (a group is all token or
-    // all weight rows: BM is a multiple of 8) and the weights are read by
-    // this workgroup alone (one token tile: decode), so it streams them with
-    // the non-temporal policy; with several token tiles the workgroups of a
-    // weight tile share it through L2 and the copy keeps the default policy.
+    // NTB: bit i set when copy i of this wave brings weight rows (a group is
+    // all token or all weight rows: BM is a multiple of 8).  Derived from the
+    // wave index through readfirstlane: the choice of copy instruction is a
+    // scalar branch and every wave issues exactly one copy per i.
     unsigned ntmask = 0;
+    if constexpr (NTB) {
 #pragma unroll
-    for (int i = 0; i < GPW; ++i)
-        if ((wave + i * NW) * 8 >= BM && p.M <= BM)
-            ntmask |= 1u << i;
-    ntmask = __builtin_amdgcn_readfirstlane(ntmask);
+        for (int i = 0; i < GPW; ++i)
+            if ((wave + i * NW) * 8 >= BM)
+                ntmask |= 1u << i;
+        ntmask = __builtin_amdgcn_readfirstlane(ntmask);
+    }
 
     static_assert(ROWS / 8 % NW == 0, "copies must split evenly over the waves");
     constexpr int L = GPW + LSC;                      // copies per wave per step
@@ -493,7 +501,7 @@ k_tile(KArgs p_)
         for (int i = 0; i < GPW; ++i) {
             const int grp_i = wave + i * NW;
             if (GROUPS % NW == 0 || grp_i < GROUPS) {
-                if ((ntmask >> i) & 1u)
+                if (NTB && ((ntmask >> i) & 1u))
                     lds_dma16_nt(src[i] + (int64_t)st * 128, dst0 + grp_i * 1024);
                 else
                     lds_dma16(src[i] + (int64_t)st * 128, dst0 + grp_i * 1024);
@@ -671,8 +679,11 @@ k_tile(KArgs p_)
 template <int FMT, int SCAL, bool SWAP, int BM, int BN, int WM, int WN, int S>
 hipError_t launch_tile(const KArgs &a, dim3 grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_tile<FMT, SCAL, SWAP, BM, BN, WM, WN, S>), grid, dim3(64 * WM * WN), 0, s,
-                       a);
+    const dim3 block(64 * WM * WN);
+    if (a.M <= BM)
+        hipLaunchKernelGGL((k_tile<FMT, SCAL, SWAP, BM, BN, WM, WN, S, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_tile<FMT, SCAL, SWAP, BM, BN, WM, WN, S, false>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 

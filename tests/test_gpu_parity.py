@@ -75,6 +75,24 @@ def test_every_instance_matches_oracle(fmt):
                 assert np.array_equal(yb, first), f"int8 variant disagreement at {c}"
 
 
+@pytest.mark.parametrize("fmt", ["int8", "fp8", "block_fp8"])
+def test_tile_instances_one_and_two_token_tiles(fmt):
+    # The tile kernel has two copy forms chosen at launch: one token tile
+    # (M <= tile_m: weight copies non-temporal) and several token tiles.
+    # Every tile instance runs both: M = tile_m - 3 and M = tile_m + 3.
+    N, K = (384, 1024)
+    for c in q.instances_for(fmt):
+        if c.kernel != q.KERNEL_TILE:
+            continue
+        for M in (c.tile_m - 3, c.tile_m + 3):
+            case = small_case(fmt, M, N, K, root=26)
+            ref = small_ref(fmt, M, N, K, root=26)
+            say("tile copy forms", fmt, M, c)
+            y = call(case, parity.to_device(case), c)
+            torch.cuda.synchronize()
+            parity.check_case(case, y, ref, what=f"{fmt} M={M} {c}")
+
+
 def test_int8_accumulators_bit_exact():
     M, N, K = SHAPE["int8"]
     case = small_case("int8", M, N, K)
