@@ -102,9 +102,15 @@ typedef enum qlin_kernel {
     QLIN_KERNEL_TILE = 1,       /* A and B tiles staged through a double-buffered LDS ring; large M */
     QLIN_KERNEL_STREAM_LDS = 2, /* weights and tokens copied HBM -> LDS in 1 KB row segments
                                    through a multi-stage ring; small M; K % 256 == 0 */
-    QLIN_KERNEL_GEMV = 3        /* one wave per weight row, dot products on the vector ALUs;
+    QLIN_KERNEL_GEMV = 3,       /* one wave per weight row, dot products on the vector ALUs;
                                    1-8 tokens (token/channel scaling) or 1-2 tokens
                                    (block scaling); split_k = 1 */
+    QLIN_KERNEL_STREAM_TOK = 4  /* one persistent workgroup per CU: the token rows of its K
+                                   range copied into LDS once, weight rows streamed through an
+                                   LDS ring; token/channel scaling, Swap-AB, 8-32 tokens per
+                                   token tile; K % 256 == 0, a split's K range at most
+                                   81920 / tile_m bytes, split_k > 1 with the two-pass
+                                   reduction; not for grouped calls */
 } qlin_kernel;
 
 typedef enum qlin_variant {
@@ -126,7 +132,9 @@ typedef enum qlin_reduce {
  * waves_n = 1 for workgroups of tile_n weight rows each, or 2 for spread
  * placement: N in 8-row units shared evenly over a grid that is a multiple
  * of the device's compute units per (token tile, split), at most tile_n
- * rows per workgroup.
+ * rows per workgroup.  For STREAM_TOK: tile_m = token rows per token tile,
+ * tile_n = 16 * waves_k weight rows per ring stage, tile_k = chunk bytes,
+ * waves_k = waves (one 16-row block each), stages = ring depth.
  * For the TILE kernel:
  * tile_m x tile_n output tile, waves_n x waves_k is the wave grid over the
  * tile (rows x columns), stages = depth of the LDS ring; tile_k = 128 is the

@@ -30,7 +30,7 @@ LIB_PATH = os.path.join(_HERE, "libqlinear.so")
 
 E4M3, INT8 = 0, 1
 TOKEN_CHANNEL, BLOCK128 = 0, 1
-KERNEL_STREAM, KERNEL_TILE, KERNEL_STREAM_LDS, KERNEL_GEMV = 0, 1, 2, 3
+KERNEL_STREAM, KERNEL_TILE, KERNEL_STREAM_LDS, KERNEL_GEMV, KERNEL_STREAM_TOK = 0, 1, 2, 3, 4
 STANDARD, SWAP_AB = 0, 1
 REDUCE_TWO_PASS, REDUCE_LAST_ARRIVER = 0, 1
 

@@ -37,6 +37,8 @@ SOURCES = [
     "qlin_stream_lds_int8.hip",
     "qlin_stream_lds_block.hip",
     "qlin_gemv.hip",
+    "qlin_stream_tok_fp8.hip",
+    "qlin_stream_tok_int8.hip",
 ]
 
 ARCH = "gfx950"

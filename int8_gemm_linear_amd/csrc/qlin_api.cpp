@@ -40,6 +40,10 @@ const int64_t kMaxLd = (int64_t(1) << 31) - 1;
 // region sits at a fixed place for every config, so partials written by one
 // config never land on the counters another config relies on being zero.
 const size_t kCounterBytes = 128 * 1024;
+// STREAM_TOK: LDS bytes for a workgroup's token rows, weight tiles per
+// workgroup at most (kTokLds / kTokTiles in qlin_stream_tok.h).
+const int64_t kTokLdsBytes = 80 * 1024;
+const int64_t kTokTiles = 4;
 const int64_t kMaxCounters = (int64_t)(kCounterBytes / 4);
 
 int fmt_bit(int fmt, int scal)
@@ -58,6 +62,7 @@ const std::vector<Instance> &registry()
             tile_instances_fp8, tile_instances_int8, tile_instances_block,
             stream_lds_instances_fp8, stream_lds_instances_int8, stream_lds_instances_block,
             tile_h_instances_fp8, tile_h_instances_int8, gemv_instances,
+            stream_tok_instances_fp8, stream_tok_instances_int8,
         };
         for (auto f : fns) {
             int n = 0;
@@ -262,6 +267,14 @@ void grid_of(const qlin_config &c, int64_t M, int64_t N, int64_t z, int64_t *gx,
     if (c.kernel == QLIN_KERNEL_TILE) {
         *gx = tn * tm;
         *gy = 1;
+    } else if (c.kernel == QLIN_KERNEL_STREAM_TOK) {
+        // one workgroup per CU over (token tile, split), enough of them that
+        // none holds more than kTokTiles tiles of 16 * waves_k rows
+        const int64_t blocks = (N + 15) / 16;
+        const int64_t per = std::max<int64_t>(1, cu_count() / (tm * std::max<int64_t>(1, z)));
+        const int64_t need = (blocks + kTokTiles * c.waves_k - 1) / (kTokTiles * c.waves_k);
+        *gx = std::max<int64_t>(1, std::min(blocks, std::max(per, need)));
+        *gy = tm;
     } else if (spread_rows(c)) {
         const int64_t units = (N + 7) / 8;
         const int64_t need = (units + c.tile_n / 8 - 1) / (c.tile_n / 8);
@@ -430,6 +443,15 @@ qlin_status check_config(int fmt, int scal, int64_t M, int64_t N, int64_t K,
         return QLIN_ERR_BAD_CONFIG;   // 256-byte K units keep the LDS swizzle in range
     if (c.kernel == QLIN_KERNEL_GEMV && c.split_k != 1)
         return QLIN_ERR_BAD_CONFIG;   // a wave covers a weight row's whole K
+    if (c.kernel == QLIN_KERNEL_STREAM_TOK) {
+        if (K % 256 != 0 || c.split_k > K / 256)
+            return QLIN_ERR_BAD_CONFIG;
+        const int64_t units = (K / 256 + c.split_k - 1) / c.split_k;
+        if (units * 256 * c.tile_m > kTokLdsBytes)
+            return QLIN_ERR_BAD_CONFIG;   // the split's token rows must fit the LDS area
+        if (c.split_k > 1 && c.reduce != QLIN_REDUCE_TWO_PASS)
+            return QLIN_ERR_BAD_CONFIG;   // partials are combined by the second pass
+    }
     int64_t gx, gy;
     grid_of(c, M, N, c.split_k, &gx, &gy);
     if (gx > 0x7fffffff || gy > 65535)
@@ -504,6 +526,8 @@ qlin_status run(const Problem &pb, const qlin_config *cfg_in)
             return QLIN_ERR_BAD_STRIDE;
         if (cfg_in && cfg_in->split_k != 1)
             return QLIN_ERR_BAD_CONFIG;   // grid.z carries the group
+        if (cfg_in && cfg_in->kernel == QLIN_KERNEL_STREAM_TOK)
+            return QLIN_ERR_BAD_CONFIG;   // its grid.z is the split and it has no group entry
     }
     const qlin_config cfg = cfg_in    ? *cfg_in
                             : grouped ? grouped_config(pb.fmt, pb.scal, pb.M, pb.N, pb.K)

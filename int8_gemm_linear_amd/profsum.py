@@ -4,6 +4,10 @@ Kernel trace (a rocprofv3 --kernel-trace output folder, csv or rocpd database):
 
     python -m int8_gemm_linear_amd.profsum trace <dir>
 
+Any counters of the GEMM kernels, per kernel, over one or more --pmc runs:
+
+    python -m int8_gemm_linear_amd.profsum counters <dir> [<dir> ...]
+
 HBM traffic per GEMM call, from two counter runs of the same bench command,
 one with ``--pmc FETCH_SIZE`` and one with ``--pmc WRITE_SIZE`` (csv output),
 each run also holding one plain copy of known size (``bench.py --copy-calib``)
@@ -180,6 +184,50 @@ def mfma_summary(folder: str, xcds: int = 8, simds: int = 1024) -> str:
     return "\n".join(lines)
 
 
+def counters_summary(folders: list[str], skip_first: int = 1) -> str:
+    """Mean value per dispatch of every counter of the GEMM kernels in one or
+    more --pmc csv runs (one run per counter pass), per kernel, leaving out
+    each kernel's first `skip_first` dispatches (cold code and TLBs); with
+    the read-latency pair, also the mean L1->L2 read latency in cycles and
+    the lines in flight per CU it implies (Little's law: requests per CU x
+    latency / GPU cycles, the GRBM count being summed over 8 XCDs)."""
+    per = collections.OrderedDict()
+    for folder in folders:
+        paths = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+        if not paths:
+            raise SystemExit(f"no counter_collection.csv under {folder}")
+        for p in paths:
+            disp = collections.OrderedDict()
+            with open(p, newline="") as f:
+                for r in csv.DictReader(f):
+                    if not _is_gemm(r["Kernel_Name"]):
+                        continue
+                    d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+                    d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            seen = collections.Counter()
+            for d in disp.values():
+                seen[d["name"]] += 1
+                if seen[d["name"]] <= skip_first:
+                    continue
+                k = per.setdefault(d["name"], collections.defaultdict(list))
+                for c, v in d.items():
+                    if c != "name":
+                        k[c].append(v)
+    lines = []
+    for name, cs in per.items():
+        m = {c: float(np.mean(v)) for c, v in cs.items()}
+        lines.append(f"== {name[:100]}")
+        req, lat = m.get("TCP_TCC_READ_REQ_sum"), m.get("TCP_TCC_READ_REQ_LATENCY_sum")
+        if req and lat:
+            line = f"   L1->L2 read latency {lat / req:.0f} cycles, {req / 256:.0f} read requests per CU"
+            if m.get("GRBM_GUI_ACTIVE"):
+                line += f", {req / 256 * (lat / req) / (m['GRBM_GUI_ACTIVE'] / 8):.0f} lines in flight per CU"
+            lines.append(line)
+        for c in sorted(m):
+            lines.append(f"   {c:42s} {m[c]:.4g}  ({len(cs[c])} dispatches)")
+    return "\n".join(lines)
+
+
 def traffic(fetch_dir: str, write_dir: str, workload: str, table: str | None) -> dict:
     out = {"workload": workload, "fingerprint": fingerprint(table)}
     for tag, folder, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
@@ -210,6 +258,8 @@ def main(argv=None):
                    help="only launches with this grid.z (e.g. the expert count of grouped calls)")
     m = sub.add_parser("mfma")
     m.add_argument("folder")
+    cs = sub.add_parser("counters")
+    cs.add_argument("folders", nargs="+")
     c = sub.add_parser("traffic")
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
@@ -224,6 +274,9 @@ def main(argv=None):
         return
     if a.cmd == "mfma":
         print(mfma_summary(a.folder))
+        return
+    if a.cmd == "counters":
+        print(counters_summary(a.folders))
         return
     rec = traffic(a.fetch, a.write, a.workload, a.table)
     if a.alg_bytes_per_call:

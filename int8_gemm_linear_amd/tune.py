@@ -50,9 +50,10 @@ def candidates(fmt: str, M: int, N: int, K: int, max_split: int = 256, kernels=N
     for base in q.instances_for(fmt):
         if kernels is not None and base.kernel not in kernels:
             continue
-        if base.kernel in (q.KERNEL_STREAM, q.KERNEL_STREAM_LDS) and -(-M // base.tile_m) > max_token_tiles:
+        lds_ring = base.kernel in (q.KERNEL_STREAM_LDS, q.KERNEL_STREAM_TOK)
+        if (base.kernel == q.KERNEL_STREAM or lds_ring) and -(-M // base.tile_m) > max_token_tiles:
             continue                      # the stream kernels are for small token counts
-        if base.kernel == q.KERNEL_STREAM_LDS and base.tile_m > 2 * M and base.tile_m > 4:
+        if lds_ring and base.tile_m > 2 * M and base.tile_m > 4:
             continue                      # a token tile mostly of padding
         if base.kernel == q.KERNEL_TILE and M < 16:
             continue
@@ -61,7 +62,7 @@ def candidates(fmt: str, M: int, N: int, K: int, max_split: int = 256, kernels=N
         split = 1
         while split <= min(max_split, 256):
             kw = base.waves_k if base.kernel == q.KERNEL_STREAM else 1
-            if split * kw > KS or (base.kernel == q.KERNEL_STREAM_LDS and split * 2 > KS):
+            if split * kw > KS or (lds_ring and split * 2 > KS):
                 break
             reds = (q.REDUCE_LAST_ARRIVER,) if split == 1 else (q.REDUCE_LAST_ARRIVER, q.REDUCE_TWO_PASS)
             for r in reds:
@@ -167,7 +168,8 @@ def grouped_candidates(fmt, M, N, K):
     """Configs a grouped call can run: split_k = 1 (grid.z is the expert),
     stream-kernel tiles of at most 4 token tiles, no spread placement."""
     return [c for c in candidates(fmt, M, N, K, max_split=1)
-            if not (c.kernel == q.KERNEL_STREAM_LDS and c.waves_n == 2)]
+            if not (c.kernel == q.KERNEL_STREAM_LDS and c.waves_n == 2)
+            and c.kernel != q.KERNEL_STREAM_TOK]
 
 
 def agree(fmt, y, ref) -> bool:
@@ -278,13 +280,18 @@ def main():
     ap.add_argument("--min-m", type=int, default=0)
     ap.add_argument("--max-m", type=int, default=1 << 30)
     ap.add_argument("--kernels", default=None, help="comma list of kernel families to sweep "
-                    "(0 stream, 1 tile, 2 LDS-ring stream, 3 GEMV); the current pick is always kept")
+                    "(0 stream, 1 tile, 2 LDS-ring stream, 3 GEMV, 4 persistent token-stationary "
+                    "stream); the current pick is always kept")
     ap.add_argument("--max-split", type=int, default=256)
     ap.add_argument("--max-token-tiles", type=int, default=4)
     ap.add_argument("--moe", default=None,
                     help="comma list of formats: sweep the grouped call on the mixture-of-experts "
                          "layers at the --moe-batches token counts")
     ap.add_argument("--moe-batches", default="1,4,16,32,64,128,512,2048")
+    ap.add_argument("--run-point", default=None,
+                    help="fmt,M,N,K: only run the library's selected config of this point --reps "
+                         "times over cold weight copies (a single-kernel program to profile)")
+    ap.add_argument("--reps", type=int, default=8)
     ap.add_argument("--min-gain", type=float, default=0.02,
                     help="keep the current pick unless the best candidate is faster by this fraction "
                          "(timings of one run differ by about that much between candidates of equal speed)")
@@ -294,6 +301,16 @@ def main():
     sys.path.insert(0, ROOT)
     import synth
 
+    if args.run_point:
+        f, M, N, K = args.run_point.split(",")
+        M, N, K = int(M), int(N), int(K)
+        pt = Point(f, M, N, K)
+        c = q.select_config(f, M, N, K)
+        for i in range(args.reps):
+            pt.call(c, i)
+        torch.cuda.synchronize()
+        print(f"[tune] ran {f} M={M} N={N} K={K} x{args.reps}: {table_line(f, M, N, K, c)}", flush=True)
+        return
     points = []
     for w in args.workload:
         points += synth.workload(w)

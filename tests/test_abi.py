@@ -410,3 +410,16 @@ def test_grouped_table_entries(tmp_path):
         assert q.config_table_size() == 3
     finally:
         q.load_config_table(None)
+
+
+def test_token_stationary_kernel_limits():
+    # the persistent token-stationary kernel: its split's token rows must fit
+    # 80 KB of LDS, split-K only with the two-pass reduction, never grouped
+    tok = [c for c in q.instances_for("int8") if c.kernel == q.KERNEL_STREAM_TOK]
+    assert tok and all(c.variant == q.SWAP_AB and c.tile_n == 16 * c.waves_k for c in tok)
+    c = [x for x in tok if x.tile_m == 32][0]
+    assert q.check_config("int8", 32, 4096, 2560, c) == 0
+    assert q.check_config("int8", 32, 4096, 2816, c) != 0
+    assert q.check_config("int8", 32, 4096, 5120, c.replace(split_k=2, reduce=q.REDUCE_TWO_PASS)) == 0
+    assert q.check_config("int8", 32, 4096, 5120, c.replace(split_k=2, reduce=q.REDUCE_LAST_ARRIVER)) != 0
+    assert not [x for x in q.instances_for("block_fp8") if x.kernel == q.KERNEL_STREAM_TOK]

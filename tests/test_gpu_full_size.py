@@ -104,3 +104,35 @@ def test_past_the_decode_range_full_size(fmt, M, N, K):
     say("boundary", fmt, (M, N, K), q.select_config(fmt, M, N, K))
     stats = run_and_check(make(fmt, M, N, K))
     say("  ok", stats)
+
+
+# The persistent token-stationary kernel at the 32B-class decode shapes, at
+# its own full-size grid (several weight tiles per workgroup), every instance
+# that takes the shape with the fewest splits its token area allows.
+TOK_POINTS = [(f, M, N, K) for f in ("int8", "fp8") for M in (16, 32)
+              for (N, K) in ((51200, 5120), (5120, 8192))]
+
+
+@pytest.mark.parametrize("fmt,M,N,K", TOK_POINTS, ids=[f"{f}-M{M}-N{N}-K{K}" for (f, M, N, K) in TOK_POINTS])
+def test_token_stationary_full_size(fmt, M, N, K):
+    case = make(fmt, M, N, K)
+    a, sa, b, sb = parity.to_device(case)
+    n = 0
+    for c in q.instances_for(fmt):
+        if c.kernel != q.KERNEL_STREAM_TOK or c.tile_m < M:
+            continue
+        def cfg(split):
+            return c.replace(split_k=split,
+                             reduce=q.REDUCE_TWO_PASS if split > 1 else q.REDUCE_LAST_ARRIVER)
+        split = 1
+        while q.check_config(fmt, M, N, K, cfg(split)) != 0:
+            split *= 2
+            assert split <= 256
+        cc = cfg(split)
+        say("token stationary full", fmt, (M, N, K), cc)
+        out = torch.full((M, N), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        q.scaled_mm(a, sa, b, sb, out=out, config=cc)
+        torch.cuda.synchronize()
+        say("  ok", parity.check_sampled(case, out, npts=1500))
+        n += 1
+    assert n > 0

@@ -362,3 +362,37 @@ def test_deep_rings_long_k(fmt):
                 yb = parity.y_bits(y)
                 first = yb if first is None else first
                 assert np.array_equal(yb, first), f"int8 disagreement at {cc}"
+
+
+@pytest.mark.parametrize("fmt", ["int8", "fp8"])
+def test_token_stationary_kernel(fmt):
+    # Persistent kernel with the token rows stationary in LDS (kernel kind 4):
+    # every instance on a one-split K (the token area at 64 KB), on a K that
+    # needs two splits for 32-token tiles (the area full for 16-token ones),
+    # and with 97 tokens (four token tiles, the last ragged) over 32 splits,
+    # which leaves 2-4 workgroups per (token tile, split): each holds up to
+    # four weight tiles of 16 * waves rows, the last one partial.
+    N = 1000
+    first = {}
+    for M, K, split in ((32, 2048, 1), (13, 5120, 2), (97, 8192, 32)):
+        case = small_case(fmt, M, N, K, root=28)
+        ref = small_ref(fmt, M, N, K, root=28)
+        dev = parity.to_device(case)
+        n = 0
+        for c in q.instances_for(fmt):
+            if c.kernel != q.KERNEL_STREAM_TOK:
+                continue
+            for s in (split, 2 * split):
+                cc = c.replace(split_k=s, reduce=q.REDUCE_TWO_PASS if s > 1 else q.REDUCE_LAST_ARRIVER)
+                if q.check_config(fmt, M, N, K, cc) != 0:
+                    continue
+                say("token stationary", fmt, (M, N, K), cc)
+                y = call(case, dev, cc)
+                torch.cuda.synchronize()
+                parity.check_case(case, y, ref, what=f"{fmt} {cc}")
+                n += 1
+                if fmt == "int8":
+                    yb = parity.y_bits(y)
+                    first.setdefault((M, K), yb)
+                    assert np.array_equal(yb, first[(M, K)]), f"int8 disagreement at {cc}"
+        assert n >= 6, n
