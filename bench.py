@@ -127,8 +127,9 @@ class Workload:
         each on the next of enough weight copies (the point's own plus
         temporary clones) that ~`cold_bytes` of distinct weights pass between
         two reads of one copy, so neither the Infinity Cache nor the L2s
-        serve the weights; replayed twice, timed with events on the launch
-        stream."""
+        serve the weights; after one untimed replay, three replays each
+        timed with events on the launch stream, the median taken (one
+        replay's window can catch the GPU in another state)."""
         import torch
         n = int(min(max_copies, max(len(it["b"]), -(-cold_bytes // (it["N"] * it["K"])))))
         bs = list(it["b"]) + [it["b"][0].clone() for _ in range(n - len(it["b"]))]
@@ -136,16 +137,17 @@ class Workload:
         g = capture(lambda: [self.call_b(it, bs[r % n]) for r in range(launches)])
         g.replay()
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (2 * launches)
+        ts = []
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / launches)
         del g, bs
-        return us
+        return float(np.median(ts))
 
     def step(self, s):
         for it in self.items:

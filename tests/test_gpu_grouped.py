@@ -113,6 +113,12 @@ def test_every_instance_grouped(fmt):
         c = cfg.replace(split_k=1, reduce=q.REDUCE_LAST_ARRIVER)
         if q.check_config(fmt, max_rows, N, K, c) != 0:
             continue
+        if c.kernel == q.KERNEL_STREAM_TOK:
+            # the persistent token-stationary kernel has no grouped form: refused
+            with pytest.raises(q.QlinError) as e:
+                run(fmt, dev, max_rows, c)
+            assert e.value.status == 6, e.value
+            continue
         say(fmt, "instance", c)
         y = run(fmt, dev, max_rows, c)
         check(fmt, y, qa, sa, qb, sb, off, max_rows, f"{fmt} {c}")

@@ -60,6 +60,8 @@ def test_every_instance_matches_oracle(fmt):
         splits = ((1, 1), (2, q.REDUCE_LAST_ARRIVER), (4, q.REDUCE_TWO_PASS))
         if cfg.kernel == q.KERNEL_GEMV:
             splits = splits[:1]               # a GEMV wave covers a row's whole K
+        if cfg.kernel == q.KERNEL_STREAM_TOK:
+            splits = ((1, 1), (2, q.REDUCE_TWO_PASS), (4, q.REDUCE_TWO_PASS))   # two-pass only
         for split, red in splits:
             c = cfg.replace(split_k=split, reduce=red)
             assert q.check_config(fmt, M, N, K, c) == 0, c
