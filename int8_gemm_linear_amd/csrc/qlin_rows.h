@@ -15,6 +15,8 @@
 // than 32768) are produced again from the L2-resident input in the
 // quantizer's second pass.  Per-group scaling needs no row reduction: the
 // 16 lanes of one 128-value group are consecutive (64W is a multiple of 16).
+// SiLU-and-mul with a per-token scale at decode sizes spreads each row over
+// several workgroups instead (k_silu_spread).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -126,11 +128,28 @@ __device__ __attribute__((noinline)) uint32_t silu_exact(float g, float u)
     return bf16_of_double((gd / (1.0 + exp(-gd))) * (double)u);
 }
 
-__device__ inline u32x4 silu8(u32x4 gw, u32x4 uw)
+// The fast path of one value: its bf16 bits from y32 in `b`; false when
+// they must come from silu_exact instead.
+__device__ inline bool silu_fast1(float g, float u, uint32_t &b)
 {
     constexpr float L_HI = 1.44269502162933349609375f;          // log2(e) rounded to fp32
     constexpr float L_LO = 1.925962989e-8f;                     // log2(e) - L_HI
     constexpr float LN2 = 0.693147180559945309f;
+    const float ng = -g;
+    const float p_hi = ng * L_HI;
+    const float p_lo = fmaf(ng, L_HI, -p_hi) + ng * L_LO;
+    const float t = __builtin_amdgcn_exp2f(p_hi) * fmaf(p_lo, LN2, 1.0f);
+    const float sv = g * __builtin_amdgcn_rcpf(1.0f + t);
+    const float y = sv * u;
+    const float as = fabsf(sv), ay = fabsf(y);
+    const uint32_t bits = __float_as_uint(y);
+    b = (bits + 0x7FFFu + ((bits >> 16) & 1u)) >> 16;
+    return fabsf(g) <= 64.0f && as >= 0x1p-100f && ay >= 0x1p-100f && ay <= 0x1p+100f &&
+           ((bits & 0xFFFFu) - 0x7FE8u) >= 48u;
+}
+
+__device__ inline u32x4 silu8(u32x4 gw, u32x4 uw)
+{
     float g[8], u[8];
     uint32_t b[8];
 #pragma unroll
@@ -142,20 +161,8 @@ __device__ inline u32x4 silu8(u32x4 gw, u32x4 uw)
     }
     uint32_t need = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float ng = -g[j];
-        const float p_hi = ng * L_HI;
-        const float p_lo = fmaf(ng, L_HI, -p_hi) + ng * L_LO;
-        const float t = __builtin_amdgcn_exp2f(p_hi) * fmaf(p_lo, LN2, 1.0f);
-        const float sv = g[j] * __builtin_amdgcn_rcpf(1.0f + t);
-        const float y = sv * u[j];
-        const float as = fabsf(sv), ay = fabsf(y);
-        const uint32_t bits = __float_as_uint(y);
-        const bool ok = fabsf(g[j]) <= 64.0f && as >= 0x1p-100f && ay >= 0x1p-100f &&
-                        ay <= 0x1p+100f && ((bits & 0xFFFFu) - 0x7FE8u) >= 48u;
-        need |= ok ? 0u : 1u << j;
-        b[j] = (bits + 0x7FFFu + ((bits >> 16) & 1u)) >> 16;
-    }
+    for (int j = 0; j < 8; ++j)
+        need |= silu_fast1(g[j], u[j], b[j]) ? 0u : 1u << j;
     if (need) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
@@ -333,6 +340,117 @@ k_rows(RowArgs a)
     }
 }
 
+// Upper bound of |bf16 SiLU-and-mul| of one value: silu(g) < g for g > 0 and
+// |silu(g)| < 0.2785 for g <= 0, so |silu(g) u| <= max(g, 0.279) |u|.  The
+// fp32 product is exact for g > 0.279 (two bf16 factors) and at most half an
+// ulp low otherwise (still above 0.2785 |u|); a NaN product, or one under
+// 2^-100 (where underflow could make it low), counts as unbounded.
+__device__ inline float silu_bound(float g, float u)
+{
+    const float b = fmaxf(g, 0.279f) * fabsf(u);
+    return b >= 0x1p-100f ? b : INFINITY;
+}
+
+// SiLU-and-mul with a per-token scale at decode sizes: a row spread over
+// several workgroups, none of which needs another's result.  At a few tokens
+// one workgroup per row leaves most CUs idle and every lane with a long
+// serial chain of SiLU and quantizer work.  Here workgroup (row, sl) of W
+// waves owns the row's pieces sl * 64W + lane, evaluated exactly (silu8) and
+// quantized; the row's scale needs the maximum |value| of the whole row,
+// which every workgroup of the row finds on its own: the maximum m of its
+// own values, then an upper bound of every other value of the row
+// (silu_bound, a multiply per value), and the exact value of only those
+// whose bound is not below m -- any other value is below m, so its bf16
+// rounding is at most m (m is a bf16 value).  Candidates are taken one value
+// per lane per pass, so a pass costs one SiLU evaluation however the
+// candidates fall; they are a few per row for real activations (the bound is
+// within a factor 1 + e^-g of the value for g > 0).  Every workgroup of a
+// row thus computes the same maximum and scale, exactly those of the
+// one-workgroup kernel.  The row is read whole by each of its workgroups
+// (from L2 after the first): a few KB per row at these sizes.
+template <int QM, int W, int PR>
+__global__ void __launch_bounds__(64 * W)
+k_silu_spread(RowArgs a)
+{
+    constexpr int NT = 64 * W;
+    constexpr bool INT8 = QM == Q_TOKEN_INT8;
+    static_assert(QM != Q_GROUP_E4M3, "per-token scaling");
+    static_assert(PR <= 16, "candidate masks");
+    const int row = blockIdx.x;
+    const int sl = blockIdx.y;
+    const int t = threadIdx.x;
+    const int P = a.K >> 3;
+    const u32x4 *x = reinterpret_cast<const u32x4 *>(a.X + (int64_t)row * a.ldx);
+    const u32x4 *up = x + P;
+    const u32x4 zero = {0, 0, 0, 0};
+    u32x4 g[PR], v[PR];
+#pragma unroll
+    for (int i = 0; i < PR; ++i) {
+        const int p = t + i * NT;
+        g[i] = p < P ? x[p] : zero;
+        v[i] = p < P ? up[p] : zero;
+    }
+    const bool own = sl * NT + t < P;
+    u32x4 yo = zero;
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PR; ++i)
+        if (i == sl && own) {
+            yo = silu8(g[i], v[i]);
+            m = amax8(yo);
+        }
+    const float mown = row_max<W>(m);
+    uint64_t cand[2] = {0, 0};           // bit 8 * (i % 8) + j of word i / 8
+#pragma unroll
+    for (int i = 0; i < PR; ++i) {
+        if (i == sl || t + i * NT >= P)
+            continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float gg = (j & 1) ? bf16_hi(g[i][j >> 1]) : bf16_lo(g[i][j >> 1]);
+            const float uu = (j & 1) ? bf16_hi(v[i][j >> 1]) : bf16_lo(v[i][j >> 1]);
+            if (!(silu_bound(gg, uu) < mown))
+                cand[i >> 3] |= 1ull << (8 * (i & 7) + j);
+        }
+    }
+    while (__any((cand[0] | cand[1]) != 0)) {
+        if (cand[0] | cand[1]) {
+            const int w = cand[0] ? 0 : 1;
+            const int k = __builtin_ctzll(cand[w]);
+            cand[w] &= cand[w] - 1;
+            const int i = 8 * w + (k >> 3), j = k & 7;
+            u32x4 gi = g[0], vi = v[0];
+#pragma unroll
+            for (int q = 1; q < PR; ++q)
+                if (q == i) {
+                    gi = g[q];
+                    vi = v[q];
+                }
+            const uint32_t gw = gi[j >> 1], uw = vi[j >> 1];
+            const float gg = (j & 1) ? bf16_hi(gw) : bf16_lo(gw);
+            const float uu = (j & 1) ? bf16_hi(uw) : bf16_lo(uw);
+            uint32_t b;
+            if (!silu_fast1(gg, uu, b))
+                b = silu_exact(gg, uu);
+            m = fmaxf(m, fabsf(__uint_as_float(b << 16)));
+        }
+    }
+    if constexpr (W > 1)
+        __syncthreads();                 // row_max's slots are written again
+    const float s = span_scale<INT8>(row_max<W>(m));
+    if (sl == 0 && t == 0)
+        a.S[row] = s;
+    if (own)
+        reinterpret_cast<uint2 *>(a.Q + (int64_t)row * a.ldq)[sl * NT + t] = quant8<INT8>(yo, s);
+}
+
+// Workgroups of k_silu_spread are 8 waves (every lane holding kReg pieces of
+// the row, so rows up to 32768 values).  Measured at 32 tokens (SiLU-and-mul
+// then per-token e4m3, K = 6144 / 12288): 2 waves per workgroup 7.07 / 7.89
+// us, 4 waves 6.85 / 7.96, 8 waves 6.75 / 7.29, one wave with 16 pieces per
+// lane 9.66 us at K = 6144; the one-workgroup-per-row kernel 7.3 / 11.1.
+constexpr int kSpreadW = 8;
+
 // Waves per row: the fewest that hold the row's pieces in registers, and
 // more while the grid has fewer than 2048 waves: with few rows (decode) the
 // per-lane work of a one-wave row is a long serial chain, so the row is
@@ -376,6 +494,15 @@ hipError_t launch_rows(const RowArgs &a, int64_t M, hipStream_t s)
     const dim3 grid((unsigned)M);
     bool skip = false;
     const int w = OP == OP_SILU ? silu_waves(M, a.K, &skip) : waves_for(M, a.K);
+    if constexpr (OP == OP_SILU && QM != Q_GROUP_E4M3) {
+        // decode sizes with a per-token scale: the row spread over workgroups
+        const int64_t P = a.K >> 3;
+        if (skip && P <= (int64_t)64 * kSpreadW * kReg) {
+            const dim3 g2((unsigned)M, (unsigned)((P + 64 * kSpreadW - 1) / (64 * kSpreadW)));
+            hipLaunchKernelGGL((k_silu_spread<QM, kSpreadW, kReg>), g2, dim3(64 * kSpreadW), 0, s, a);
+            return hipGetLastError();
+        }
+    }
     if constexpr (OP == OP_SILU) {
         if (skip) {
             switch (w) {

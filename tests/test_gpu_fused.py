@@ -222,3 +222,37 @@ def test_fused_equals_unfused_library_path():
     qf, sf, _ = run_rms(x, w, "int8", False)
     assert np.array_equal(codes(qu), qf)
     assert same_scales(su.cpu().numpy(), sf)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("K", [6144, 6160, 25600])
+def test_silu_rows_spread_over_workgroups(fmt, K):
+    # At a few tokens a per-token SiLU-and-mul row is spread over several
+    # workgroups, each of which finds the row maximum itself (its own exact
+    # values, then the exact value of every other value whose bound reaches
+    # them).  Rows built so the maximum sits where that search must find it:
+    # an all-zero row (every bound is a candidate), a maximum through the
+    # double path (gate > 64) in the last workgroup's slice, a maximum from a
+    # negative gate with a large up value, the maximum value twice in two
+    # slices, a maximum in the first slice, and a random row.  K = 6160 makes
+    # the last slice two pieces long.
+    rng = np.random.default_rng(61)
+    M = 6
+    g = synth.bf16_round(rng.normal(0.0, 0.01, (M, K)).astype(np.float32))
+    u = synth.bf16_round(rng.normal(0.0, 0.01, (M, K)).astype(np.float32))
+    g[0] = 0.0
+    u[0] = 0.0
+    g[1, K - 3], u[1, K - 3] = 100.0, 3.0
+    g[2, K // 2 + 5], u[2, K // 2 + 5] = -1.28125, 1000.0
+    g[3, 11], u[3, 11] = 2.5, -7.0
+    g[3, K - 40], u[3, K - 40] = 2.5, 7.0
+    g[4, 3], u[4, 3] = 5.0, 5.0
+    g[5] = synth.bf16_round(rng.normal(0.0, 1.0, K).astype(np.float32))
+    u[5] = synth.bf16_round(rng.normal(0.0, 1.0, K).astype(np.float32))
+    x = np.concatenate([g, u], axis=1)
+    say("silu spread", fmt, M, K)
+    qd, sd = q.silu_and_mul_dynamic_per_token_quant(dev(x), TORCH_DT[fmt])
+    torch.cuda.synchronize()
+    qr, sr = oracle.silu_and_mul_quant(x, ORC_DT[fmt], 0)
+    assert same_scales(sd.cpu().numpy(), sr)
+    assert np.array_equal(codes(qd), qr)
