@@ -39,6 +39,7 @@ SOURCES = [
     "qlin_gemv.hip",
     "qlin_stream_tok_fp8.hip",
     "qlin_stream_tok_int8.hip",
+    "qlin_stream_own.hip",
 ]
 
 ARCH = "gfx950"

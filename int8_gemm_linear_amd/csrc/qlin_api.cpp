@@ -62,7 +62,7 @@ const std::vector<Instance> &registry()
             tile_instances_fp8, tile_instances_int8, tile_instances_block,
             stream_lds_instances_fp8, stream_lds_instances_int8, stream_lds_instances_block,
             tile_h_instances_fp8, tile_h_instances_int8, gemv_instances,
-            stream_tok_instances_fp8, stream_tok_instances_int8,
+            stream_tok_instances_fp8, stream_tok_instances_int8, stream_own_instances,
         };
         for (auto f : fns) {
             int n = 0;
