@@ -1,5 +1,6 @@
 // Wide-row form of the STREAM_LDS family (tile_k = 256): one workgroup per
-// CU holds up to TR = 128 or 256 weight rows and every token row of its tile.
+// CU holds up to TR = 128 or 256 weight rows and every token row of its tile
+// (16-32 tokens).
 //
 // Why: at 16-32 tokens each workgroup of the LDS ring copies its token rows
 // once per K range, so the token bytes a CU copies per weight byte are
