@@ -128,7 +128,9 @@ typedef enum qlin_reduce {
  * each wave loads per pipeline step (multiple of 128), waves_n x waves_k
  * waves split the tile's rows and the split's K range.  For STREAM_LDS:
  * tile_m / tile_n as for STREAM, tile_k = bytes per row per LDS chunk (512
- * or 1024), waves_k waves share each chunk's K steps, stages = ring depth,
+ * or 1024), waves_k waves share each chunk's K steps, stages = ring depth;
+ * tile_k = 256 is the wide-row form (Swap-AB only, tile_n = 128 or 256 rows,
+ * each of the waves_k waves owning whole 16-row blocks for every K step),
  * waves_n = 1 for workgroups of tile_n weight rows each, or 2 for spread
  * placement: N in 8-row units shared evenly over a grid that is a multiple
  * of the device's compute units per (token tile, split), at most tile_n
