@@ -398,3 +398,36 @@ def test_token_stationary_kernel(fmt):
                     first.setdefault((M, K), yb)
                     assert np.array_equal(yb, first[(M, K)]), f"int8 disagreement at {cc}"
         assert n >= 6, n
+
+
+@pytest.mark.parametrize("fmt", ["int8", "fp8", "block_fp8"])
+def test_wide_row_kernel_at_its_placement(fmt):
+    # The wide-row LDS ring (tile_k = 256) as the table uses it on N = 51200:
+    # spread placement gives 256 workgroups of 200 rows each, starting at
+    # multiples of 8 that are not multiples of 128, so a workgroup's rows
+    # span up to three 128-row weight blocks (Block_FP8 scales).  Short K
+    # keeps the oracle fast while every output element is compared; 16, 24
+    # and 32 tokens, with and without split-K.
+    N, K = 51200, 1024
+    cfgs = [c for c in q.instances_for(fmt)
+            if c.kernel == q.KERNEL_STREAM_LDS and c.tile_k == 256 and c.waves_n == 2]
+    assert {c.tile_n for c in cfgs} == {128, 256}, cfgs
+    first = {}
+    for M in (16, 24, 32):
+        case = small_case(fmt, M, N, K, root=29)
+        ref = small_ref(fmt, M, N, K, root=29)
+        dev = parity.to_device(case)
+        for c in cfgs:
+            if c.tile_m < M and -(-M // c.tile_m) > 2:
+                continue
+            for split, red in ((1, 1), (2, q.REDUCE_TWO_PASS), (4, q.REDUCE_LAST_ARRIVER)):
+                cc = c.replace(split_k=split, reduce=red)
+                assert q.check_config(fmt, M, N, K, cc) == 0, cc
+                say("wide rows", fmt, (M, N, K), cc)
+                y = call(case, dev, cc)
+                torch.cuda.synchronize()
+                parity.check_case(case, y, ref, what=f"{fmt} {cc}")
+                if fmt == "int8":
+                    yb = parity.y_bits(y)
+                    first.setdefault(M, yb)
+                    assert np.array_equal(yb, first[M]), f"int8 disagreement at {cc}"
