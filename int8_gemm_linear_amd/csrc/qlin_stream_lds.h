@@ -567,6 +567,10 @@ hipError_t launch_stream_lds(const KArgs &a, dim3 grid, hipStream_t s)
     QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 2),      \
     QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 4),      \
     QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 8),      \
+    X(FMT, BIT, SW, 2, 32, 8, 3, 1024),            \
+    X(FMT, BIT, SW, 4, 32, 8, 3, 1024),            \
+    X(FMT, BIT, SW, 8, 32, 8, 2, 1024),            \
+    X(FMT, BIT, SW, 8, 32, 8, 3, 1024),            \
     QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 16),     \
     QLIN_STREAM_LDS_RING(X, FMT, BIT, SW, 32),     \
     X(FMT, BIT, SW, 16, 32, 4, 2, 1024),           \
