@@ -245,11 +245,14 @@ __device__ inline __attribute__((always_inline)) void tile_finish(const KArgs &p
     // and written back as whole 16-byte pieces of contiguous rows, so every
     // store instruction covers full 128-byte lines of Y instead of 32 rows x
     // 16 bytes.  Row stride BN*2 bytes; the CPR 16-byte chunks of a row are
-    // XOR-swizzled by the row index against LDS bank conflicts.
+    // permuted by the row index against LDS bank conflicts: XOR-swizzled when
+    // CPR is a power of two, else rotated by the row index.
     constexpr int CPR = BN / 8;                       // 16-byte chunks per row
-    static_assert((CPR & (CPR - 1)) == 0, "chunks per row");
+    constexpr bool CPR2 = (CPR & (CPR - 1)) == 0;
     constexpr int NT = 64 * WM * WN;
-    auto stage_off = [&](int r, int c) { return r * (BN * 2) + 16 * (c ^ (r & (CPR - 1))); };
+    auto stage_off = [&](int r, int c) {
+        return r * (BN * 2) + 16 * (CPR2 ? (c ^ (r & (CPR - 1))) : (c + r) % CPR);
+    };
     auto emit_staged = [&](const A16 (&val)[FM][FN]) {
         __syncthreads();                               // every wave is done with the ring
         if (SWAP) {
@@ -692,6 +695,8 @@ hipError_t launch_tile(const KArgs &a, dim3 grid, hipStream_t s)
      &launch_tile<FMT, SCAL, (SW) != 0, BM, BN, WM, WN, S>}
 
 // (BM, BN, WM, WN, S) for token/channel scaling; LDS = S * (BM + BN) * 128 B.
+// 256 x 160 gives N = 5120 at M = 2048 exactly 256 tiles (one per CU; a
+// 256 x 256 tile leaves 96 CUs idle there).
 #define QLIN_TILE_SHAPES(X, FMT, SCAL, BIT, SW) \
     X(FMT, SCAL, BIT, SW, 64, 128, 1, 4, 4),    \
     X(FMT, SCAL, BIT, SW, 64, 128, 2, 4, 4),    \
@@ -705,7 +710,8 @@ hipError_t launch_tile(const KArgs &a, dim3 grid, hipStream_t s)
     X(FMT, SCAL, BIT, SW, 256, 256, 2, 4, 2),   \
     X(FMT, SCAL, BIT, SW, 256, 256, 4, 2, 2),   \
     X(FMT, SCAL, BIT, SW, 256, 128, 4, 2, 3),   \
-    X(FMT, SCAL, BIT, SW, 128, 256, 2, 4, 3)
+    X(FMT, SCAL, BIT, SW, 128, 256, 2, 4, 3),   \
+    X(FMT, SCAL, BIT, SW, 256, 160, 4, 1, 3)
 
 // Block scaling (the stage also carries the step's scales, under 2 KB).
 #define QLIN_TILE_SHAPES_BLOCK(X, FMT, SCAL, BIT, SW) \
