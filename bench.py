@@ -414,13 +414,25 @@ def moe_points(reps: int = 8, target_bytes: int = 1 << 30):
 
 
 def cpu_model() -> str:
+    """The host CPU's model name, with its family / model / stepping numbers
+    (some hosts report only a generic name)."""
+    name, ids = "unknown", {}
     try:
         for ln in open("/proc/cpuinfo"):
-            if ln.startswith("model name"):
-                return ln.split(":", 1)[1].strip()
+            key, _, val = ln.partition(":")
+            key = key.strip()
+            if key == "model name" and name == "unknown":
+                name = val.strip()
+            elif key in ("cpu family", "model", "stepping") and key not in ids:
+                ids[key] = val.strip()
+            elif not ln.strip() and name != "unknown":
+                break
     except OSError:
         pass
-    return "unknown"
+    if ids:
+        name += " (family %s, model %s, stepping %s)" % (
+            ids.get("cpu family", "?"), ids.get("model", "?"), ids.get("stepping", "?"))
+    return name
 
 
 def dispatch_cost():
